@@ -1,0 +1,355 @@
+"""Pins for the fp64 oracle: each check is fixed by the mathematics, a library
+routine, a brute force or a closed form, never by the oracle itself.
+
+Runs on the CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as gen
+import oracle
+from oracle import brute
+
+
+def _draw(rng, shape, dtype, scale=1.0):
+    return gen.round_bits(rng.standard_normal(shape).astype(np.float32) * scale, dtype)
+
+
+def _f(bits, dtype):
+    return gen.bits_to_float(bits, dtype).astype(np.float64)
+
+
+# ------------------------------------------------------------ decoding ----
+
+def test_widen_f16_every_pattern_matches_numpy():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def test_widen_bf16_every_pattern_matches_torch():
+    import torch
+
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+# --------------------------------------------------------- brute force ----
+
+def _brute_case(rng, B, H, Nq, Nk, d, dtype, causal, kv_lens, scale):
+    q = _draw(rng, (B, H, Nq, d), dtype)
+    k = _draw(rng, (B, H, Nk, d), dtype)
+    v = _draw(rng, (B, H, Nk, d), dtype)
+    o, lse = oracle.attention_fwd(q, k, v, dtype, scale, causal, kv_lens)
+    qf, kf, vf = _f(q, dtype), _f(k, dtype), _f(v, dtype)
+    for b in range(B):
+        for h in range(H):
+            bo, bl = brute.attention(qf[b, h].tolist(), kf[b, h].tolist(), vf[b, h].tolist(),
+                                     scale, causal,
+                                     None if kv_lens is None else int(kv_lens[b]))
+            bo, bl = np.array(bo), np.array(bl)
+            fin = np.isfinite(bl)
+            assert np.array_equal(fin, np.isfinite(lse[b, h]))
+            assert np.all(lse[b, h][~fin] == -np.inf)
+            assert np.max(np.abs(lse[b, h][fin] - bl[fin]), initial=0) <= 1e-12
+            assert np.max(np.abs(o[b, h] - bo), initial=0) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_matches_brute_force(seed, dtype, causal):
+    rng = np.random.default_rng(seed + 100 * causal)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    Nq, Nk, d = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    kv_lens = None
+    if seed % 2:
+        kv_lens = rng.integers(0, Nk + 2, size=B).astype(np.int32)   # includes 0 and > Nk
+    _brute_case(rng, B, H, Nq, Nk, d, dtype, causal, kv_lens, 1.0 / math.sqrt(d))
+
+
+def test_oracle_matches_brute_force_square_causal_padded():
+    rng = np.random.default_rng(7)
+    _brute_case(rng, 2, 2, 8, 8, 8, "bf16", True, np.array([8, 3], np.int32), 0.35)
+
+
+# --------------------------------------------------------- closed forms ---
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_that_constant(causal):
+    rng = np.random.default_rng(1)
+    q = _draw(rng, (2, 2, 16, 8), "bf16")
+    k = _draw(rng, (2, 2, 16, 8), "bf16")
+    for c in [2.0, -0.5, 0.7109375]:
+        v = gen.float_to_bits_exact(np.full((2, 2, 16, 8), c, np.float32), "bf16")
+        o, _ = oracle.attention_fwd(q, k, v, "bf16", 0.3, causal, np.array([16, 9], np.int32))
+        # the probabilities sum to one up to a few fp64 roundings
+        assert np.max(np.abs(o - c)) <= 16 * 2.0 ** -52 * abs(c)
+
+
+def _zero_q_case(Nq, Nk, causal, kv_lens, B=2):
+    rng = np.random.default_rng(3)
+    d = 4
+    q = np.zeros((B, 1, Nq, d), np.uint16)
+    k = _draw(rng, (B, 1, Nk, d), "f16")
+    v = _draw(rng, (B, 1, Nk, d), "f16")
+    o, lse = oracle.attention_fwd(q, k, v, "f16", 0.5, causal, kv_lens)
+    vf = _f(v, "f16")
+    for b in range(B):
+        n_b = Nk if kv_lens is None else min(int(kv_lens[b]), Nk)
+        for i in range(Nq):
+            n = n_b
+            if causal:
+                n = min(n, max(0, i + Nk - Nq + 1))
+            if n == 0:
+                assert lse[b, 0, i] == -np.inf and np.all(o[b, 0, i] == 0)
+                continue
+            assert abs(lse[b, 0, i] - math.log(n)) <= 1e-14
+            np.testing.assert_allclose(o[b, 0, i], vf[b, 0, :n].mean(axis=0), rtol=0,
+                                       atol=1e-14)
+
+
+def test_zero_q_uniform_attention_noncausal():
+    _zero_q_case(5, 7, False, None)
+
+
+def test_zero_q_uniform_attention_causal_square():
+    _zero_q_case(9, 9, True, None)
+
+
+def test_zero_q_uniform_attention_causal_bottom_right():
+    _zero_q_case(4, 10, True, None)      # Nq < Nk: row i sees keys j <= i + 6
+    _zero_q_case(10, 4, True, None)      # Nq > Nk: first rows see nothing
+
+
+def test_zero_q_uniform_attention_padding():
+    _zero_q_case(6, 12, False, np.array([12, 5], np.int32))
+    _zero_q_case(12, 12, True, np.array([7, 0], np.int32))
+
+
+def test_causal_row0_is_v0():
+    rng = np.random.default_rng(5)
+    q = _draw(rng, (1, 3, 32, 16), "bf16")
+    k = _draw(rng, (1, 3, 32, 16), "bf16")
+    v = _draw(rng, (1, 3, 32, 16), "bf16")
+    o, lse = oracle.attention_fwd(q, k, v, "bf16", 0.25, True)
+    qf, kf, vf = _f(q, "bf16"), _f(k, "bf16"), _f(v, "bf16")
+    assert np.array_equal(o[0, :, 0], vf[0, :, 0])
+    s00 = 0.25 * np.einsum("ht,ht->h", qf[0, :, 0], kf[0, :, 0])
+    np.testing.assert_allclose(lse[0, :, 0], s00, rtol=0, atol=1e-14)
+
+
+def test_single_query_causal_equals_noncausal():
+    rng = np.random.default_rng(6)
+    q = _draw(rng, (2, 2, 1, 16), "f16")
+    k = _draw(rng, (2, 2, 40, 16), "f16")
+    v = _draw(rng, (2, 2, 40, 16), "f16")
+    a = oracle.attention_fwd(q, k, v, "f16", 0.25, True)
+    b = oracle.attention_fwd(q, k, v, "f16", 0.25, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_two_key_worked_case():
+    # d=1, scale=1, q=1, k=(0,1): P=(1/(1+e), e/(1+e)), LSE=ln(1+e)
+    q = gen.float_to_bits_exact(np.ones((1, 1, 1, 1), np.float32), "f16")
+    k = gen.float_to_bits_exact(np.array([0.0, 1.0], np.float32).reshape(1, 1, 2, 1), "f16")
+    v0, v1 = 3.0, -5.0
+    v = gen.float_to_bits_exact(np.array([v0, v1], np.float32).reshape(1, 1, 2, 1), "f16")
+    o, lse = oracle.attention_fwd(q, k, v, "f16", 1.0, False)
+    e = math.e
+    assert abs(o[0, 0, 0, 0] - (v0 + e * v1) / (1 + e)) <= 1e-15
+    assert abs(lse[0, 0, 0] - math.log(1 + e)) <= 1e-15
+
+
+def test_shift_of_keys_shifts_lse_only():
+    """Adding u to every key adds scale*q_i.u to every score of row i: O is
+    unchanged and LSE moves by exactly that amount.  u is chosen so that the
+    shifted scores reach ~+100 (exp overflows float32 there without a max shift)."""
+    rng = np.random.default_rng(8)
+    B, H, N, d = 1, 2, 24, 8
+    # values on a 1/16 grid, |x| <= 4, so K+u stays exact in f16
+    grid = lambda shape: np.round(rng.uniform(-4, 4, shape) * 16) / 16
+    qf = grid((B, H, N, d)).astype(np.float32)
+    kf = grid((B, H, N, d)).astype(np.float32)
+    vf = grid((B, H, N, d)).astype(np.float32)
+    u = np.full(d, 50.0, np.float32)
+    q = gen.float_to_bits_exact(qf, "f16")
+    k = gen.float_to_bits_exact(kf, "f16")
+    k2 = gen.float_to_bits_exact(kf + u, "f16")
+    v = gen.float_to_bits_exact(vf, "f16")
+    scale = 0.5
+    for causal in (False, True):
+        o1, l1 = oracle.attention_fwd(q, k, v, "f16", scale, causal)
+        o2, l2 = oracle.attention_fwd(q, k2, v, "f16", scale, causal)
+        shift = scale * (qf.astype(np.float64) @ u.astype(np.float64))
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l2, l1 + shift, rtol=1e-14, atol=1e-12)
+        assert np.max(l2) > 100
+
+
+def test_needle_key_selects_its_value():
+    rng = np.random.default_rng(9)
+    B, H, N, d = 1, 1, 64, 16
+    qf = gen.bits_to_float(_draw(rng, (B, H, N, d), "bf16"), "bf16")
+    kf = gen.bits_to_float(_draw(rng, (B, H, N, d), "bf16"), "bf16") * 0.01
+    i, jstar = 40, 17
+    kf[0, 0, jstar] = qf[0, 0, i] * 64.0            # exact in bf16 (power-of-two scale)
+    q = gen.float_to_bits_exact(qf, "bf16")
+    k = gen.round_bits(kf, "bf16")
+    v = _draw(rng, (B, H, N, d), "bf16")
+    o, _ = oracle.attention_fwd(q, k, v, "bf16", 1.0, True)
+    np.testing.assert_allclose(o[0, 0, i], _f(v, "bf16")[0, 0, jstar], atol=1e-9)
+
+
+def test_affine_in_v():
+    rng = np.random.default_rng(10)
+    B, H, N, d = 2, 2, 20, 8
+    q = _draw(rng, (B, H, N, d), "f16")
+    k = _draw(rng, (B, H, N, d), "f16")
+    grid = lambda: (np.round(rng.uniform(-8, 8, (B, H, N, d)) * 8) / 8).astype(np.float32)
+    v1f, v2f = grid(), grid()
+    v1 = gen.float_to_bits_exact(v1f, "f16")
+    v2 = gen.float_to_bits_exact(v2f, "f16")
+    vc = gen.float_to_bits_exact(2 * v1f - 3 * v2f + 1.0, "f16")
+    kl = np.array([20, 11], np.int32)
+    o1, l1 = oracle.attention_fwd(q, k, v1, "f16", 0.4, True, kl)
+    o2, _ = oracle.attention_fwd(q, k, v2, "f16", 0.4, True, kl)
+    oc, lc = oracle.attention_fwd(q, k, vc, "f16", 0.4, True, kl)
+    np.testing.assert_allclose(oc, 2 * o1 - 3 * o2 + 1.0, rtol=0, atol=1e-12)
+    assert np.array_equal(lc, l1)
+
+
+def test_split_keys_combine_by_lse_rule():
+    """Attention over all keys equals the LSE-weighted merge of attention over
+    two disjoint key blocks (the recurrence that online softmax and split-KV
+    decode both rest on)."""
+    rng = np.random.default_rng(11)
+    B, H, Nq, Nk, d = 1, 2, 5, 30, 16
+    q = _draw(rng, (B, H, Nq, d), "bf16")
+    k = _draw(rng, (B, H, Nk, d), "bf16")
+    v = _draw(rng, (B, H, Nk, d), "bf16")
+    cut = 13
+    of, lf = oracle.attention_fwd(q, k, v, "bf16", 0.25, False)
+    o1, l1 = oracle.attention_fwd(q, k[:, :, :cut], v[:, :, :cut], "bf16", 0.25, False)
+    o2, l2 = oracle.attention_fwd(q, k[:, :, cut:], v[:, :, cut:], "bf16", 0.25, False)
+    m = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - m), np.exp(l2 - m)
+    om = (w1[..., None] * o1 + w2[..., None] * o2) / (w1 + w2)[..., None]
+    lm = m + np.log(w1 + w2)
+    np.testing.assert_allclose(om, of, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lf, rtol=0, atol=1e-12)
+
+
+def test_identity_v_gives_scipy_softmax_rows():
+    """With V = identity (d = Nk) each output row is the softmax of the scaled
+    score row itself; compare with scipy's softmax and logsumexp."""
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(12)
+    N = 16
+    q = _draw(rng, (1, 1, N, N), "f16")
+    k = _draw(rng, (1, 1, N, N), "f16")
+    v = gen.float_to_bits_exact(np.eye(N, dtype=np.float32).reshape(1, 1, N, N), "f16")
+    scale = 0.3
+    o, lse = oracle.attention_fwd(q, k, v, "f16", scale, False)
+    s = scale * (_f(q, "f16")[0, 0] @ _f(k, "f16")[0, 0].T)
+    np.testing.assert_allclose(o[0, 0], softmax(s, axis=1), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s, axis=1), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o[0, 0].sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_row_subset_matches_full_rows():
+    w = gen.fwd_inputs(2, 3, 40, 40, 16, "bf16", 77, causal=True, scale=0.125,
+                       kv_len_range=(10, 40))
+    o, lse = oracle.attention_fwd(w.q, w.k, w.v, "bf16", w.scale, True, w.kv_lens)
+    rows = np.array([239, 0, 5, 119, 120, 77], np.int64)
+    os_, ls_ = oracle.attention_fwd(w.q, w.k, w.v, "bf16", w.scale, True, w.kv_lens, rows=rows)
+    assert np.array_equal(os_, o.reshape(-1, 16)[rows])
+    assert np.array_equal(ls_, lse.reshape(-1)[rows])
+
+
+def test_thread_count_does_not_change_bits():
+    w = gen.fwd_inputs(2, 3, 33, 47, 16, "f16", 78, causal=True, scale=0.2)
+    a = oracle.attention_fwd(w.q, w.k, w.v, "f16", w.scale, True, nthreads=1)
+    b = oracle.attention_fwd(w.q, w.k, w.v, "f16", w.scale, True, nthreads=5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- decode ---
+
+def _tiny_decode(identity=False, seed=21):
+    return gen.decode_inputs(3, 2, 8, (1, 37), "bf16", seed, page_size=4, num_pages=64,
+                             identity_pages=identity)
+
+
+def test_decode_matches_brute_force():
+    inp = _tiny_decode()
+    o, lse = oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, "bf16", inp.scale)
+    qf, kf, vf = _f(inp.q, "bf16"), _f(inp.k, "bf16"), _f(inp.v, "bf16")
+    for s in range(inp.S):
+        a, b = inp.seq_off[s], inp.seq_off[s + 1]
+        for h in range(inp.H):
+            bo, bl = brute.attention([qf[s, h].tolist()], kf[a:b, h].tolist(),
+                                     vf[a:b, h].tolist(), inp.scale)
+            assert abs(bl[0] - lse[s, h]) <= 1e-12
+            assert np.max(np.abs(np.array(bo[0]) - o[s, h])) <= 1e-12
+
+
+def test_decode_zero_query_is_mean_of_cache():
+    inp = _tiny_decode(seed=22)
+    qz = np.zeros_like(inp.q)
+    o, lse = oracle.decode(qz, inp.k, inp.v, inp.seq_off, "bf16", inp.scale)
+    vf = _f(inp.v, "bf16")
+    for s in range(inp.S):
+        a, b = inp.seq_off[s], inp.seq_off[s + 1]
+        np.testing.assert_allclose(o[s], vf[a:b].mean(axis=0), atol=1e-14, rtol=0)
+        np.testing.assert_allclose(lse[s], math.log(b - a), atol=1e-14, rtol=0)
+
+
+def test_page_pool_round_trip():
+    inp = _tiny_decode(seed=23)
+    nan_bf16 = 0x7FC0
+    for which, src in (("k", inp.k), ("v", inp.v)):
+        pool = gen.build_pool_host(inp, which, fill_bits=nan_bf16)
+        assert np.array_equal(gen.gather_logical(pool, inp), src)
+        used = np.zeros(pool.shape[0] * pool.shape[2], bool)
+        phys, row = gen.page_slots(inp)
+        used[phys * inp.page_size + row] = True
+        slots = pool.transpose(0, 2, 1, 3).reshape(-1, inp.H, inp.d)
+        assert np.all(slots[~used] == nan_bf16)
+    # each logical page maps to a distinct physical page
+    t = inp.page_table[inp.page_table >= 0]
+    assert len(np.unique(t)) == len(t)
+
+
+def test_decode_on_gathered_pool_equals_logical():
+    inp = _tiny_decode(seed=24)
+    kp = gen.build_pool_host(inp, "k")
+    vp = gen.build_pool_host(inp, "v")
+    a = oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, "bf16", inp.scale)
+    b = oracle.decode(inp.q, gen.gather_logical(kp, inp), gen.gather_logical(vp, inp),
+                      inp.seq_off, "bf16", inp.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_decode_equals_forward_with_one_query():
+    inp = _tiny_decode(seed=25)
+    o, lse = oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, "bf16", inp.scale)
+    for s in range(inp.S):
+        a, b = inp.seq_off[s], inp.seq_off[s + 1]
+        kk = np.ascontiguousarray(inp.k[a:b].transpose(1, 0, 2))[None]
+        vv = np.ascontiguousarray(inp.v[a:b].transpose(1, 0, 2))[None]
+        fo, fl = oracle.attention_fwd(inp.q[s][None, :, None, :], kk, vv, "bf16", inp.scale,
+                                      True)
+        np.testing.assert_allclose(fo[0, :, 0], o[s], atol=1e-15, rtol=0)
+        np.testing.assert_allclose(fl[0, :, 0], lse[s], atol=1e-15, rtol=0)
