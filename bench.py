@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs
+already resident in HBM:
+  * fa_fwd on the causal B=8, H=16, N=4096, d=64 bf16 forward (the workload
+    the headline TFLOP/s is quoted on), and
+  * fa_decode_paged on the decode batch (32 sequences x 32 heads, d=128,
+    lengths uniform in [512, 8192], 16-token pages scattered over a
+    65536-page pool).
+Each kernel is bracketed by HIP events on the stream it is launched on.
+
+Prints ONE JSON line.  ``value`` is forward TFLOP/s (nominal FLOPs
+4*B*H*Nq*Nk*d, halved for causal, over the forward's average event time);
+``roofline`` is the forward kernel against the dense bf16 MFMA peak;
+``decode`` carries the decode GB/s against the 8 TB/s HBM peak; and
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+forward workload on the host cores (and reports the sample's parity).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import fa_inputs as gen  # noqa: E402
+
+FWD_WORKLOAD = "fwd_causal_b8h16_n4096_d64_bf16"
+DEC_WORKLOAD = "decode_paged_s32h32_d128_bf16"
+
+# MI355X published peaks (dense, no sparsity)
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_causal_b8h16_n4096_d64.json")
+FWD_SOURCE = os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", "fa_fwd.hip")
+
+
+def attention_flops(B, H, Nq, Nk, d, causal):
+    """Nominal FLOPs: 4*B*H*Nq*Nk*d, halved for causal (gpu-inference page,
+    section 02: symmetric accounting; work skipped at the diagonal is not
+    credited and work done on the diagonal tiles is not counted twice)."""
+    f = 4.0 * B * H * Nq * Nk * d
+    return f * 0.5 if causal else f
+
+
+def decode_bytes(kv_lens, H, d, elem=2, with_io=True):
+    """Algorithmic bytes of one decode call: every cached K and V element once,
+    plus q, o (fp32), lse (fp32), the page-table entries used and kv_lens."""
+    tokens = int(np.sum(kv_lens))
+    b = 2 * tokens * H * d * elem
+    if with_io:
+        S = len(kv_lens)
+        pages = int(np.sum((np.asarray(kv_lens) + 15) // 16))
+        b += S * H * d * elem + S * H * d * 4 + S * H * 4 + pages * 4 + S * 4
+    return b
+
+
+def fwd_bytes(B, H, Nq, Nk, d, elem=2):
+    """Compulsory HBM bytes of the forward: Q, K, V once, O (fp32) and LSE once."""
+    return B * H * (Nq + 2 * Nk) * d * elem + B * H * Nq * d * 4 + B * H * Nq * 4
+
+
+def kernel_digest():
+    h = hashlib.sha256()
+    for name in ("fa_fwd.hip", "fa_common.h"):
+        with open(os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter runs,
+    or None if they were taken on a different version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
+    """Time the fp64 oracle on a bounded sample of query rows of the forward
+    workload (uniformly drawn rows, so the sample has the workload's mix of
+    causal row lengths).  Returns the baseline dict."""
+    import oracle
+
+    B, H, Nq, Nk, d = w.shape
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(seed)
+
+    def run(nrows):
+        rows = np.unique(rng.integers(0, B * H * Nq, size=nrows))
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal,
+                                              w.kv_lens, rows=rows, nthreads=cores)
+        dt = time.perf_counter() - t0
+        i = rows % Nq
+        n_valid = np.minimum(i + 1, Nk) if w.causal else np.full(rows.shape, Nk)
+        flops = float(np.sum(4.0 * d * n_valid))
+        return rows, o_ref, lse_ref, dt, flops
+
+    rows, o_ref, lse_ref, dt, flops = run(256 * cores)
+    if dt < target_s:
+        want = int(len(rows) * min(target_s / max(dt, 1e-3), 64.0))
+        rows, o_ref, lse_ref, dt, flops = run(min(want, B * H * Nq))
+    og = o_gpu.reshape(-1, d)[rows].astype(np.float64)
+    lg = lse_gpu.reshape(-1)[rows].astype(np.float64)
+    err = np.abs(og - o_ref)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{len(rows)} uniformly drawn query rows of {B * H * Nq} "
+                  f"({FWD_WORKLOAD}), fp64, {dt:.1f} s",
+        "seconds": dt,
+        "sample_parity": {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                          "lse_rel": float(np.max(np.abs(lg - lse_ref) /
+                                                  np.maximum(1, np.abs(lse_ref))))},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true", help="time the forward only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by batch/head with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    fa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] generating {FWD_WORKLOAD}", file=sys.stderr, flush=True)
+    w = gen.fwd_workload(FWD_WORKLOAD)
+    B, H, Nq, Nk, d = w.shape
+    q, k, v = (gen.to_torch(x, w.dtype).to(dev) for x in (w.q, w.k, w.v))
+    o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    fflops = attention_flops(B, H, Nq, Nk, d, w.causal)
+
+    dec = None
+    if not args.no_decode:
+        print(f"[bench] generating {DEC_WORKLOAD}", file=sys.stderr, flush=True)
+        dec = gen.decode_workload(DEC_WORKLOAD)
+        kp = gen.build_pool_device(dec, "k", dev)
+        vp = gen.build_pool_device(dec, "v", dev)
+        dq = gen.to_torch(dec.q, dec.dtype).to(dev)
+        dpt = torch.from_numpy(dec.page_table).to(dev)
+        dkl = torch.from_numpy(dec.kv_lens).to(dev)
+        do = torch.empty((dec.S, dec.H, dec.d), dtype=torch.float32, device=dev)
+        dlse = torch.empty((dec.S, dec.H), dtype=torch.float32, device=dev)
+        ws_bytes = fa.fa_decode_workspace_bytes(dec.S, dec.H, dec.d, dec.page_table.shape[1], 16)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        dbytes = decode_bytes(dec.kv_lens, dec.H, dec.d)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        fa.forward(q, k, v, scale=w.scale, causal=True, out=(o, lse))
+        if evs is not None:
+            evs[1].record()
+        if dec is not None:
+            fa.decode_paged(dq, kp, vp, dpt, dkl, scale=dec.scale, workspace=ws, out=(do, dlse))
+            if evs is not None:
+                evs[2].record()
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    fwd_avg_s = float(fwd_ms.mean()) / 1e3
+    tflops = fflops / fwd_avg_s / 1e12
+    result = {
+        "metric": "attention fwd TFLOP/s (causal B8 H16 d64 N4096) + % MFMA peak; decode GB/s",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": FWD_WORKLOAD, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d,
+                   "causal": True, "decode_workload": None if dec is None else DEC_WORKLOAD},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic()},
+        "fwd": {"kernel_ms_avg": float(fwd_ms.mean()), "kernel_ms_p10": float(np.percentile(fwd_ms, 10)),
+                "kernel_ms_p90": float(np.percentile(fwd_ms, 90)), "flops": fflops,
+                "compulsory_bytes": fwd_bytes(B, H, Nq, Nk, d)},
+    }
+    if dec is not None:
+        dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+        gbs = dbytes / (float(dec_ms.mean()) / 1e3) / 1e9
+        result["decode"] = {
+            "GB/s": gbs, "kernel_ms_avg": float(dec_ms.mean()),
+            "kernel_ms_p10": float(np.percentile(dec_ms, 10)),
+            "kernel_ms_p90": float(np.percentile(dec_ms, 90)),
+            "bytes": dbytes, "tokens": int(dec.kv_lens.sum()),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+        }
+    if args.cpu_seconds > 0:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, o.cpu().numpy(), lse.cpu().numpy(),
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

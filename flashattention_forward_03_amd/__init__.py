@@ -1,0 +1,232 @@
+"""Python binding of the gfx950 exact-attention library (``libfa_mi355x.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/fa.h``.  PyTorch provides
+device memory and the current stream.  There is no CPU path: if the library
+is missing or no GPU is present, calls raise.
+
+Two layers:
+  * ``fa_fwd``, ``fa_decode_paged``, ``fa_decode_workspace_bytes``,
+    ``fa_status_str``, ``fa_last_hip_error``: the C entry points with the same
+    names and arguments (raw device addresses as ints, stream as int).
+  * ``forward`` / ``decode_paged``: take torch tensors, check them, allocate
+    the outputs (and the decode workspace), call the entry point on the
+    current stream and raise ``FAError`` on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_UNSUPPORTED = 3
+FA_ERR_ALIGN = 4
+FA_ERR_WORKSPACE = 5
+FA_ERR_HIP = 6
+FA_ERR_ARG = 7
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+
+EXPORTED = ("fa_fwd", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_str",
+            "fa_last_hip_error", "fa_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where}: status {status} ({fa_status_str(status)})"
+        if status == FA_ERR_HIP:
+            msg += f", hipError {fa_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+def load_library():
+    """Load ``libfa_mi355x.so`` (built by ``flashattention_forward_03_amd.build``).
+
+    torch is imported first when it is installed: torch ships its own HIP
+    runtime, and the library must bind to that same runtime (loaded first,
+    the library would pull in a second HIP/HSA runtime and the process would
+    hold two).  Raises if two HIP runtimes end up mapped.
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m flashattention_forward_03_amd.build")
+    try:
+        import torch  # noqa: F401  (binds the process to torch's HIP runtime first)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process: " + ", ".join(runtimes))
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P]
+    lib.fa_fwd.restype = I
+    lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fa_decode_paged.restype = I
+    lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_decode_workspace_bytes.restype = Z
+    lib.fa_status_str.argtypes = [I]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = I
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = I
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------ C entry points
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_lens, dtype, stream) -> int:
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_lens, dtype,
+                                 stream)
+
+
+def fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
+                    max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes,
+                    stream) -> int:
+    return load_library().fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H,
+                                          d, page_size, max_pages_per_seq, num_pages, scale,
+                                          dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size) -> int:
+    return int(load_library().fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size))
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def fa_last_hip_error() -> int:
+    return int(load_library().fa_last_hip_error())
+
+
+# ------------------------------------------------------------ torch wrappers
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _check_dev(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
+            kv_lens=None, stream=None, out=None):
+    """Exact attention forward on [B, H, N, d] f16/bf16 tensors.
+
+    Returns ``(o, lse)``: o float32 [B, H, Nq, d], lse float32 [B, H, Nq].
+    ``kv_lens``: optional int32 GPU tensor [B] of valid key counts.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl_ptr = None
+    if kv_lens is not None:
+        _check_dev("kv_lens", kv_lens)
+        if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+            raise ValueError("kv_lens must be int32 [B]")
+        kl_ptr = kv_lens.data_ptr()
+    if out is None:
+        o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                Nk, d, float(scale), int(bool(causal)), kl_ptr, dt, _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[float] = None,
+                 workspace=None, stream=None, out=None):
+    """Decode attention: q [S, H, d], pools [num_pages, H, page_size, d],
+    page_table int32 [S, max_pages], kv_lens int32 [S].  Returns (o, lse)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("page_table", page_table), ("kv_lens", kv_lens)):
+        _check_dev(name, t)
+    S, H, d = q.shape
+    num_pages, Hp, page_size, dp = k_pages.shape
+    if (Hp, dp) != (H, d) or v_pages.shape != k_pages.shape:
+        raise ValueError("pools must be [num_pages, H, page_size, d] matching q")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != S:
+        raise ValueError("page_table must be int32 [S, max_pages]")
+    if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (S,):
+        raise ValueError("kv_lens must be int32 [S]")
+    dt = _dtype_code(q)
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the pools must share one dtype")
+    max_pages = page_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_bytes(S, H, d, max_pages, page_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if out is None:
+        o = torch.empty((S, H, d), dtype=torch.float32, device=q.device)
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                         page_table.data_ptr(), kv_lens.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         S, H, d, page_size, max_pages, num_pages, float(scale), dt, ws_ptr,
+                         ws_bytes, _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_paged")
+    return o, lse

@@ -1,0 +1,149 @@
+// C-ABI layer: argument checks (all before any HIP call), workspace sizing,
+// dispatch to the kernel launchers, HIP error capture.  See include/fa.h.
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("FA_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    g_last_hip_error = (int)e;
+    if (log_enabled())
+        std::fprintf(stderr, "fa: %s failed: %s\n", what, hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+size_t decode_ws_bytes(long long S, long long H, long long d, int max_pages)
+{
+    const long long chunks = fa::decode_max_chunks(max_pages);
+    if (chunks <= 1)
+        return 0;
+    return (size_t)(S * H * chunks * d * 4 + S * H * chunks * 2 * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 1; }
+
+const char *fa_status_str(int status)
+{
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid size (negative, or too large to index)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim, page size or dtype";
+    case FA_ERR_ALIGN: return "pointer not aligned as required";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP launch failed";
+    case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0; causal 0 or 1)";
+    default: return "unknown status";
+    }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int Nq,
+           int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1)
+        return FA_ERR_ARG;
+    if (!scale_ok(scale))
+        return FA_ERR_ARG;
+    if (B == 0 || H == 0 || Nq == 0)
+        return FA_OK;
+    if (fa::fwd_grid_size(B, H, Nq) > INT_MAX)
+        return FA_ERR_SHAPE;
+    if (!q || !o || !lse || (Nk > 0 && (!k || !v)))
+        return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(kv_lens, 4))
+        return FA_ERR_ALIGN;
+
+    fa::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal == 1, dtype == FA_DTYPE_BF16, kv_lens};
+    const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_fwd launch");
+    return FA_OK;
+}
+
+size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size)
+{
+    if (S < 0 || H < 0 || (d != 64 && d != 128) || max_pages_per_seq < 1 || page_size != 16)
+        return 0;
+    return decode_ws_bytes(S, H, d, max_pages_per_seq);
+}
+
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                    const int32_t *kv_lens, float *o, float *lse, int S, int H, int d, int page_size,
+                    int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    if (S < 0 || H < 0 || max_pages_per_seq < 1 || num_pages < 1)
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128)
+        return FA_ERR_UNSUPPORTED;
+    if (page_size != 16)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (!scale_ok(scale))
+        return FA_ERR_ARG;
+    if ((long long)max_pages_per_seq * page_size > INT_MAX)
+        return FA_ERR_SHAPE;
+    if (S == 0 || H == 0)
+        return FA_OK;
+    if ((long long)S * H * fa::decode_max_chunks(max_pages_per_seq) > INT_MAX)
+        return FA_ERR_SHAPE;
+    if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !o || !lse)
+        return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16) ||
+        !aligned(page_table, 4) || !aligned(kv_lens, 4) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const size_t need = decode_ws_bytes(S, H, d, max_pages_per_seq);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16))
+            return FA_ERR_ALIGN;
+    }
+    const long long chunks = fa::decode_max_chunks(max_pages_per_seq);
+    float *part_o = need ? static_cast<float *>(workspace) : nullptr;
+    float *part_ml = need ? part_o + (size_t)S * H * chunks * d : nullptr;
+
+    fa::DecodeArgs a{q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
+                     max_pages_per_seq, num_pages, scale, dtype == FA_DTYPE_BF16, part_o, part_ml};
+    const hipError_t e = fa::launch_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_decode_paged launch");
+    return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,271 @@
+// Decode attention over a paged KV cache for gfx950 (MI355X).
+//
+// One query per (sequence, head) attends to every cached token of its
+// sequence; token t of sequence s sits in page page_table[s][t / 16], row
+// t % 16 (inference kernel cookbook page, recipe 03 "Paged Attention": fixed
+// size pages reached through a page table, scattered physical pages giving
+// the same result).  The arithmetic is the forward's with one query row:
+// scores, online softmax (running max and normaliser, NanoInfer page "Online
+// Softmax"), rescaled accumulation of p * V.
+//
+// The work is bandwidth bound (one FMA per byte of K/V), so there is no MFMA
+// here: the kernel is laid out for HBM streaming.
+//   * Split-KV: one workgroup per (sequence, head, chunk of 32 pages = 512
+//     tokens) so that ~S*H*len/512 workgroups fill the 256 CUs even when a
+//     batch mixes short and long sequences.  Chunk boundaries depend only on
+//     logical token positions.
+//   * 256 threads: token row r = tid / (d/8), 8 consecutive head dims per
+//     thread; a (page, head) block of 16 x d bf16 is contiguous in the pool,
+//     so each step is one fully coalesced 16-byte load per thread for K and
+//     one for V.  Several steps are loaded before any is used to keep bytes
+//     in flight.
+//   * q.k is reduced over the d/8 lanes of a row with DPP moves; every thread
+//     keeps its own online-softmax state for its token stream; the streams
+//     are merged through LDS at the end of the chunk with the log-sum-exp
+//     rule.
+//   * Chunks of one (sequence, head) are merged by a second small kernel with
+//     the same rule; a sequence with a single chunk is finished directly.
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int PAGE = 16;
+constexpr int NTHREADS = 256;
+constexpr int STEPS_IN_FLIGHT = 4;
+
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), result in all of them.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row_mirror
+    return x;
+}
+
+// Sum over aligned groups of 8 lanes.
+__device__ __forceinline__ float row8_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    return x;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen8(const u32x4_t &w, float *f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = lo16<BF16>(w[i]);
+        f[2 * i + 1] = hi16<BF16>(w[i]);
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
+    const uint16_t *__restrict__ Qp, const uint16_t *__restrict__ Kp, const uint16_t *__restrict__ Vp,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ kv_lens, float *__restrict__ O,
+    float *__restrict__ LSE, float *__restrict__ part_o, float *__restrict__ part_ml, int H, int max_pages,
+    int num_pages, int max_chunks, float c_log2)
+{
+    constexpr int TPR = D / 8;                 // threads per token row
+    constexpr int ROWS = NTHREADS / TPR;       // token rows per step (16 or 32)
+    constexpr int PPS = ROWS / PAGE;           // pages per step (1 or 2)
+    constexpr int CHUNK = kDecodeChunkPages;
+    static_assert(PPS >= 1 && CHUNK % PPS == 0, "step must tile the chunk");
+
+    __shared__ float sm_m[ROWS], sm_l[ROWS];
+    __shared__ float sm_o[ROWS][D + 4];
+
+    const int chunk = blockIdx.x % max_chunks;
+    const int sh = blockIdx.x / max_chunks;
+    const int s = sh / H, h = sh - s * H;
+
+    int kvlen = kv_lens[s];
+    kvlen = kvlen < 0 ? 0 : (kvlen > max_pages * PAGE ? max_pages * PAGE : kvlen);
+    const int npages = (kvlen + PAGE - 1) / PAGE;
+    const int nchunks = (npages + CHUNK - 1) / CHUNK;
+    if (chunk >= nchunks)
+        return;
+    const int p_begin = chunk * CHUNK;
+    const int p_end = min(p_begin + CHUNK, npages);
+    const int nsteps = (p_end - p_begin + PPS - 1) / PPS;
+
+    const int tid = threadIdx.x;
+    const int r = tid / TPR;           // token row within a step
+    const int gd = tid - r * TPR;      // which 8 head dims
+    const int page_in_step = r / PAGE;
+    const int row_in_page = r % PAGE;
+
+    float qv[8];
+    widen8<BF16>(load16(Qp + (size_t)sh * D + 8 * gd), qv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        qv[i] *= c_log2;
+
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = 0.f;
+
+    const int32_t *pt = page_table + (size_t)s * max_pages;
+    const size_t head_off = (size_t)h * PAGE * D + (size_t)row_in_page * D + 8 * gd;
+    const size_t page_stride = (size_t)H * PAGE * D;
+
+    for (int k0 = 0; k0 < nsteps; k0 += STEPS_IN_FLIGHT) {
+        u32x4_t kr[STEPS_IN_FLIGHT], vr[STEPS_IN_FLIGHT];
+        bool ok[STEPS_IN_FLIGHT];
+#pragma unroll
+        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
+            const int page = p_begin + (k0 + u) * PPS + page_in_step;
+            const int tok = page * PAGE + row_in_page;
+            ok[u] = (k0 + u < nsteps) && page < p_end && tok < kvlen;
+            if (ok[u]) {
+                int phys = pt[page];
+                phys = phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+                const size_t off = (size_t)phys * page_stride + head_off;
+                kr[u] = load16(Kp + off);
+                vr[u] = load16(Vp + off);
+            } else {
+                kr[u] = u32x4_t{0, 0, 0, 0};
+                vr[u] = u32x4_t{0, 0, 0, 0};
+            }
+        }
+        float t[STEPS_IN_FLIGHT];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
+            float kf[8];
+            widen8<BF16>(kr[u], kf);
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                dot = fmaf(qv[i], kf[i], dot);
+            dot = (TPR == 16) ? row16_sum(dot) : row8_sum(dot);
+            t[u] = ok[u] ? dot : -INFINITY;
+            mx = fmaxf(mx, t[u]);
+        }
+        const float m_new = fmaxf(m, mx);
+        if (m_new == -INFINITY)
+            continue;
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
+            const float p = fast_exp2(t[u] - m_new);
+            l += p;
+            float vf[8];
+            widen8<BF16>(vr[u], vf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = fmaf(p, vf[i], acc[i]);
+        }
+        m = m_new;
+    }
+
+    // ---- merge the ROWS token streams of this chunk
+    if (gd == 0) {
+        sm_m[r] = m;
+        sm_l[r] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        sm_o[r][8 * gd + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+        float M = -INFINITY;
+        for (int j = 0; j < ROWS; ++j)
+            M = fmaxf(M, sm_m[j]);
+        float L = 0.f, num = 0.f;
+        for (int j = 0; j < ROWS; ++j) {
+            const float w = sm_m[j] == -INFINITY ? 0.f : fast_exp2(sm_m[j] - M);
+            L = fmaf(w, sm_l[j], L);
+            num = fmaf(w, sm_o[j][tid], num);
+        }
+        if (nchunks == 1) {
+            O[(size_t)sh * D + tid] = num / L;
+            if (tid == 0)
+                LSE[sh] = (M + __log2f(L)) * kLn2;
+        } else {
+            const size_t slot = (size_t)sh * max_chunks + chunk;
+            part_o[slot * D + tid] = num;
+            if (tid == 0) {
+                part_ml[2 * slot] = M;
+                part_ml[2 * slot + 1] = L;
+            }
+        }
+    }
+}
+
+// Merge the chunk partials of each (sequence, head); write empty sequences.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const int32_t *__restrict__ kv_lens,
+                                                           const float *__restrict__ part_o,
+                                                           const float *__restrict__ part_ml,
+                                                           float *__restrict__ O, float *__restrict__ LSE,
+                                                           int H, int max_pages, int max_chunks)
+{
+    const int sh = blockIdx.x;
+    const int s = sh / H;
+    int kvlen = kv_lens[s];
+    kvlen = kvlen < 0 ? 0 : (kvlen > max_pages * PAGE ? max_pages * PAGE : kvlen);
+    const int npages = (kvlen + PAGE - 1) / PAGE;
+    const int nchunks = (npages + kDecodeChunkPages - 1) / kDecodeChunkPages;
+    const int tid = threadIdx.x;
+    if (nchunks == 1)
+        return;
+    if (nchunks == 0) {
+        O[(size_t)sh * D + tid] = 0.f;
+        if (tid == 0)
+            LSE[sh] = -INFINITY;
+        return;
+    }
+    const float *ml = part_ml + (size_t)sh * max_chunks * 2;
+    const float *po = part_o + (size_t)sh * max_chunks * D;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunks; ++c)
+        M = fmaxf(M, ml[2 * c]);
+    float L = 0.f, num = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+        const float w = fast_exp2(ml[2 * c] - M);
+        L = fmaf(w, ml[2 * c + 1], L);
+        num = fmaf(w, po[(size_t)c * D + tid], num);
+    }
+    O[(size_t)sh * D + tid] = num / L;
+    if (tid == 0)
+        LSE[sh] = (M + __log2f(L)) * kLn2;
+}
+
+template <int D, bool BF16>
+hipError_t launch(const DecodeArgs &a, hipStream_t stream)
+{
+    const int max_chunks = decode_max_chunks(a.max_pages);
+    const long long grid = (long long)a.S * a.H * max_chunks;
+    hipLaunchKernelGGL((decode_split_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k_pages, (const uint16_t *)a.v_pages,
+                       a.page_table, a.kv_lens, a.o, a.lse, a.part_o, a.part_ml, a.H, a.max_pages,
+                       a.num_pages, max_chunks, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.S * a.H)), dim3(D), 0, stream,
+                       a.kv_lens, a.part_o, a.part_ml, a.o, a.lse, a.H, a.max_pages, max_chunks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
+{
+    if (a.d == 64)
+        return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+}
+
+}  // namespace fa

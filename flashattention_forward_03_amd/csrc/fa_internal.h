@@ -1,0 +1,38 @@
+// Internal launcher interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    float *o, *lse;
+    int B, H, Nq, Nk, d;
+    float scale;
+    bool causal, bf16;
+    const int32_t *kv_lens;
+};
+
+struct DecodeArgs {
+    const void *q, *k_pages, *v_pages;
+    const int32_t *page_table, *kv_lens;
+    float *o, *lse;
+    int S, H, d, page_size, max_pages, num_pages;
+    float scale;
+    bool bf16;
+    float *part_o, *part_ml;   // workspace views (NULL when one chunk covers every sequence)
+};
+
+// Forward: number of workgroups one call launches.
+long long fwd_grid_size(int B, int H, int Nq);
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+
+// Decode: cached tokens per split-KV chunk, and the launch.
+constexpr int kDecodeChunkPages = 32;
+inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,145 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * Two operations, both asynchronous on the caller's HIP stream:
+ *
+ *   fa_fwd           exact attention forward: O = softmax(scale * Q K^T + mask) V
+ *                    and the per-row log-sum-exp, computed tile by tile with an
+ *                    online softmax so that the Nq x Nk score matrix never
+ *                    exists in memory.  Definition: Kernel-Inference-Engine
+ *                    page, attention-block chart (softmax(QK^T/sqrt(d))) and
+ *                    tile dataflow chart (S = Q_i K_j^T scale, mask, online
+ *                    softmax with running max and normaliser, rescale of the
+ *                    O accumulator, O += P V_j, normalise and store); masks
+ *                    as on the gpu-inference page, section 02 (causal mask
+ *                    combined with the padding mask before the softmax);
+ *                    the saved log-sum-exp statistic of that same section.
+ *
+ *   fa_decode_paged  one query per (sequence, head) attending to every cached
+ *                    token of its sequence, the cache stored in fixed-size
+ *                    pages found through a page table (inference kernel
+ *                    cookbook page, recipe 03 "Paged Attention"; NanoInfer
+ *                    page, paged KV-cache allocator).  Same definition with
+ *                    query length 1.
+ *
+ * Conventions (after the Kernel-Inference-Engine page's op sequence chart:
+ * the framework allocates outputs and workspace, raw device pointers plus the
+ * stream go to the launch, no host round trip, no private allocation, error
+ * read back right after the launch; and its design note that the op has no
+ * CPU kernel):
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees, copies to/from the host or synchronises.
+ *   - `stream` is a hipStream_t passed as void*; NULL = the null stream.
+ *   - Calls return once the kernels are enqueued.  Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - Argument checks all happen before any HIP call, so a rejected call
+ *     has no side effect.  Values that live in device memory (kv_lens,
+ *     page_table) cannot be checked without a sync: kernels clamp them into
+ *     range so that they never read or write outside the buffers whose sizes
+ *     the arguments describe; results for out-of-contract values are
+ *     unspecified.
+ *   - Results are a pure function of the inputs: bitwise reproducible from
+ *     run to run.
+ *   - Thread safety: calls may be made concurrently from several threads.
+ *     fa_last_hip_error() is per thread.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FA_OK 0
+#define FA_ERR_NULL 1        /* a required pointer is NULL */
+#define FA_ERR_SHAPE 2       /* a size is negative, or a product overflows the index range */
+#define FA_ERR_UNSUPPORTED 3 /* head dim, page size or dtype not built */
+#define FA_ERR_ALIGN 4       /* a pointer is not aligned as stated below */
+#define FA_ERR_WORKSPACE 5   /* workspace missing or smaller than fa_decode_workspace_bytes */
+#define FA_ERR_HIP 6         /* a HIP launch failed; see fa_last_hip_error() */
+#define FA_ERR_ARG 7         /* scale not finite and > 0, or causal not 0/1 */
+
+/* element types of Q, K, V (and the KV pools) */
+#define FA_DTYPE_F16 0
+#define FA_DTYPE_BF16 1
+
+/*
+ * Exact attention forward.
+ *
+ *   q        [B, H, Nq, d]  f16/bf16 (dtype), contiguous, d innermost; 16-byte aligned
+ *   k, v     [B, H, Nk, d]  same dtype and layout; 16-byte aligned
+ *   o        [B, H, Nq, d]  float32 output (written); 16-byte aligned
+ *   lse      [B, H, Nq]     float32 output (written): natural log of the sum of
+ *                           exp(scaled scores) over the row's valid keys;
+ *                           4-byte aligned
+ *   d        64 or 128
+ *   scale    multiplies Q.K (finite, > 0; typically 1/sqrt(d))
+ *   causal   0 or 1.  Query row i may see key j only if j <= i + (Nk - Nq)
+ *            (aligned at the bottom-right; plain lower-triangular when Nq == Nk)
+ *   kv_lens  NULL (all Nk keys valid) or a device int32 [B]: keys j >= kv_lens[b]
+ *            are masked for every head and query row of batch b.  Values are
+ *            clamped to [0, Nk].
+ *
+ * A row with no valid key gets O = 0 and LSE = -inf.  B, H or Nq of 0 is an
+ * empty problem (FA_OK, nothing written, pointers may be NULL).  Nk = 0 is
+ * allowed (every row empty).  The library needs no workspace for this call.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
+           int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype,
+           void *stream);
+
+/*
+ * Decode attention over a paged KV cache (query length 1).
+ *
+ *   q           [S, H, d] f16/bf16; 16-byte aligned
+ *   k_pages,
+ *   v_pages     [num_pages, H, page_size, d] pools, same dtype; 16-byte aligned.
+ *               Token t of sequence s lives in page page_table[s][t / page_size],
+ *               row t % page_size.
+ *   page_table  device int32 [S, max_pages_per_seq]; entries beyond a sequence's
+ *               pages are ignored (never read).  4-byte aligned
+ *   kv_lens     device int32 [S]: number of cached tokens of each sequence, all of
+ *               which the query attends to.  Clamped to [0, max_pages_per_seq *
+ *               page_size].  A used table entry outside [0, num_pages) is clamped
+ *               into range (result unspecified, no out-of-bounds access).
+ *   o           [S, H, d] float32 output; 16-byte aligned
+ *   lse         [S, H] float32 output; 4-byte aligned
+ *   d           64 or 128;  page_size 16
+ *   workspace   device buffer of at least
+ *               fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size)
+ *               bytes, 16-byte aligned, owned by the caller; its contents on
+ *               entry do not matter.  NULL allowed only if that size is 0.
+ *
+ * A sequence with kv_len 0 gets O = 0 and LSE = -inf.  S or H of 0 is an empty
+ * problem.  Long sequences are split into chunks of cached tokens whose
+ * partial results are merged with the log-sum-exp rule; the split depends
+ * only on logical token positions, so the result does not depend on where the
+ * pages sit in the pool.
+ */
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *page_table, const int32_t *kv_lens, float *o, float *lse,
+                    int S, int H, int d, int page_size, int max_pages_per_seq, int num_pages,
+                    float scale, int dtype, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Workspace bytes fa_decode_paged needs for these sizes (0 for invalid sizes). */
+size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size);
+
+/* Static, human-readable text for a status code. */
+const char *fa_status_str(int status);
+
+/* The hipError_t of this thread's most recent FA_ERR_HIP (0 if none). */
+int fa_last_hip_error(void);
+
+/* Library version, for the binding's sanity check. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

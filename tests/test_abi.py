@@ -1,0 +1,147 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fa.h declares,
+and rejects bad arguments before any HIP call (no GPU needed)."""
+import os
+import re
+
+import pytest
+
+import flashattention_forward_03_amd as fa
+from flashattention_forward_03_amd import build as fabuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    fabuild.build(force=False)
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {fa.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings(lib):
+    assert fa.load_library().fa_version() == 1
+    for code in range(0, 8):
+        s = fa.fa_status_str(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_str(99) == "unknown status"
+    assert fa.fa_last_hip_error() == 0
+
+
+A = 0x10000          # fake, 16-byte aligned addresses: never dereferenced on these paths
+GOOD = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0,
+            kv_lens=None, dtype=1, stream=None)
+
+
+def call_fwd(**over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                     a["d"], a["scale"], a["causal"], a["kv_lens"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+    (dict(Nk=-3), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_ARG),
+    (dict(scale=-0.125), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(k=None), fa.FA_ERR_NULL),
+    (dict(q=A + 8), fa.FA_ERR_ALIGN),
+    (dict(v=A + 2), fa.FA_ERR_ALIGN),
+    (dict(o=A + 4), fa.FA_ERR_ALIGN),
+    (dict(lse=A + 2), fa.FA_ERR_ALIGN),
+    (dict(kv_lens=A + 1), fa.FA_ERR_ALIGN),
+    (dict(B=0x10000, H=0x10000, Nq=0x10000), fa.FA_ERR_SHAPE),
+    # empty problems: nothing to do, no pointer needed, no HIP call
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
+    (dict(H=0, q=None, o=None, lse=None), fa.FA_OK),
+    (dict(Nq=0, q=None, o=None, lse=None), fa.FA_OK),
+])
+def test_fwd_argument_checks(lib, over, status):
+    assert call_fwd(**over) == status
+
+
+GOOD_DEC = dict(q=A, kp=A, vp=A, pt=A, kl=A, o=A, lse=A, S=2, H=2, d=128, page_size=16,
+                max_pages=100, num_pages=64, scale=0.088, dtype=1, ws=A, ws_bytes=1 << 30,
+                stream=None)
+
+
+def call_dec(**over):
+    a = dict(GOOD_DEC)
+    a.update(over)
+    return fa.fa_decode_paged(a["q"], a["kp"], a["vp"], a["pt"], a["kl"], a["o"], a["lse"], a["S"],
+                              a["H"], a["d"], a["page_size"], a["max_pages"], a["num_pages"],
+                              a["scale"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_decode_workspace_size(lib):
+    # 100 pages -> 4 chunks of 32 pages; per (s,h,chunk): d floats + (max, sum)
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 16) == 2 * 2 * 4 * (128 + 2) * 4
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 32, 16) == 0      # one chunk: none needed
+    assert fa.fa_decode_workspace_bytes(2, 2, 96, 100, 16) == 0      # unsupported -> 0
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 8) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(S=-1), fa.FA_ERR_SHAPE),
+    (dict(max_pages=0), fa.FA_ERR_SHAPE),
+    (dict(num_pages=0), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(page_size=8), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_ARG),
+    (dict(pt=None), fa.FA_ERR_NULL),
+    (dict(kl=None), fa.FA_ERR_NULL),
+    (dict(kp=A + 2), fa.FA_ERR_ALIGN),
+    (dict(pt=A + 2), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=2 * 2 * 4 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.FA_ERR_ALIGN),
+    (dict(S=0, q=None, o=None), fa.FA_OK),
+])
+def test_decode_argument_checks(lib, over, status):
+    assert call_dec(**over) == status
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(x, x, x)
+
+
+def test_binding_keeps_one_hip_runtime_in_the_process():
+    """Loading the library must not map a second HIP runtime next to torch's
+    (two HIP/HSA runtimes in one process crash torch's own GPU calls)."""
+    import subprocess
+    import sys
+
+    code = ("import flashattention_forward_03_amd as fa; fa.load_library(); "
+            "import torch; print(len(fa._hip_runtimes_mapped()))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True)
+    assert out.stdout.strip() == "1"

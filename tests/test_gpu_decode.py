@@ -1,0 +1,138 @@
+"""GPU parity of fa_decode_paged against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import fa_inputs as gen
+import oracle
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+NAN_F16 = 0x7E00
+
+
+def run_decode(inp: gen.DecodeInputs, fill_bits=0, pools=None):
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    dev = "cuda"
+    if pools is None:
+        kp = gen.build_pool_device(inp, "k", dev, fill_bits)
+        vp = gen.build_pool_device(inp, "v", dev, fill_bits)
+    else:
+        kp, vp = pools
+    q = gen.to_torch(inp.q, inp.dtype).to(dev)
+    pt = torch.from_numpy(inp.page_table).to(dev)
+    kl = torch.from_numpy(inp.kv_lens).to(dev)
+    o, lse = fa.decode_paged(q, kp, vp, pt, kl, scale=inp.scale)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def ref_decode(inp):
+    return oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, inp.dtype, inp.scale)
+
+
+@pytest.fixture(scope="module")
+def big():
+    """The full decode batch: 32 sequences x 32 heads, d=128, lengths 512..8192,
+    pages scattered over a 65536-page pool (the pools are built once)."""
+    inp = gen.decode_workload("decode_paged_s32h32_d128_bf16")
+    pools = (gen.build_pool_device(inp, "k", "cuda"), gen.build_pool_device(inp, "v", "cuda"))
+    yield inp, pools
+    del pools
+
+
+def test_full_decode_parity(big):
+    big, pools = big
+    o, lse = run_decode(big, pools=pools)
+    o_ref, lse_ref = ref_decode(big)
+    stats = compare(o, lse, o_ref, lse_ref, "decode s32 h32 d128")
+    print("decode", stats, flush=True)
+
+
+def test_paged_equals_identity_table_bitwise(big):
+    """Scattered pages and pages laid out in logical order give the same bits."""
+    big, pools = big
+    ident = gen.decode_workload("decode_paged_s32h32_d128_bf16", identity_pages=True)
+    assert np.array_equal(ident.k, big.k)
+    o1, l1 = run_decode(big, pools=pools)
+    o2, l2 = run_decode(ident)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("S,H,d,lens,dtype,num_pages", [
+    (5, 3, 128, (1, 40), "bf16", 64),            # < 1 page, ragged last page
+    (4, 2, 128, (500, 530), "f16", 256),          # around one chunk (512 tokens)
+    (3, 2, 64, (1, 1500), "bf16", 512),           # d = 64, several chunks
+    (2, 4, 64, (2000, 2100), "f16", 512),
+    (7, 1, 128, (16, 16), "bf16", 16),            # exactly one page each
+])
+def test_small_decode_parity(S, H, d, lens, dtype, num_pages):
+    inp = gen.decode_inputs(S, H, d, lens, dtype, seed=S * 100 + d + lens[1],
+                            page_size=16, num_pages=num_pages)
+    o, lse = run_decode(inp)
+    o_ref, lse_ref = ref_decode(inp)
+    compare(o, lse, o_ref, lse_ref, f"decode S{S} H{H} d{d} lens{lens} {dtype}")
+
+
+def test_unused_slots_poisoned_with_nan_do_not_leak():
+    for dtype, nan in (("bf16", NAN_BF16), ("f16", NAN_F16)):
+        inp = gen.decode_inputs(6, 2, 128, (1, 700), dtype, seed=77, page_size=16,
+                                num_pages=512)
+        o, lse = run_decode(inp, fill_bits=nan)
+        o_ref, lse_ref = ref_decode(inp)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        compare(o, lse, o_ref, lse_ref, f"poisoned {dtype}")
+
+
+def test_zero_length_sequence():
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    inp = gen.decode_inputs(3, 2, 128, (5, 900), "bf16", seed=78, page_size=16, num_pages=256)
+    kp = gen.build_pool_device(inp, "k", "cuda")
+    vp = gen.build_pool_device(inp, "v", "cuda")
+    lens = inp.kv_lens.copy()
+    lens[1] = 0
+    q = gen.to_torch(inp.q, "bf16").cuda()
+    o, lse = fa.decode_paged(q, kp, vp, torch.from_numpy(inp.page_table).cuda(),
+                             torch.from_numpy(lens).cuda(), scale=inp.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    o_ref, lse_ref = ref_decode(inp)
+    for s in (0, 2):
+        compare(o[s], lse[s], o_ref[s], lse_ref[s], f"seq {s}")
+
+
+def test_decode_matches_forward_with_one_query():
+    """Decode over pages == fa_fwd with Nq = 1 over the same cache gathered
+    into a contiguous [1, H, L, d] tensor on the host (within the parity bar)."""
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    inp = gen.decode_inputs(4, 4, 128, (100, 3000), "bf16", seed=79, page_size=16,
+                            num_pages=1024)
+    o, lse = run_decode(inp)
+    for s in range(inp.S):
+        a, b = inp.seq_off[s], inp.seq_off[s + 1]
+        kk = torch.from_numpy(np.ascontiguousarray(inp.k[a:b].transpose(1, 0, 2))[None].view(np.int16))
+        vv = torch.from_numpy(np.ascontiguousarray(inp.v[a:b].transpose(1, 0, 2))[None].view(np.int16))
+        qq = torch.from_numpy(np.ascontiguousarray(inp.q[s][None, :, None, :]).view(np.int16))
+        fo, fl = fa.forward(qq.view(torch.bfloat16).cuda(), kk.view(torch.bfloat16).cuda(),
+                            vv.view(torch.bfloat16).cuda(), scale=inp.scale, causal=True)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(fo.cpu().numpy()[0, :, 0] - o[s])) <= 1e-2
+        assert np.max(np.abs(fl.cpu().numpy()[0, :, 0] - lse[s])) <= 1e-3 * max(1, np.abs(lse[s]).max())
+
+
+def test_decode_deterministic(big):
+    big, pools = big
+    o1, l1 = run_decode(big, pools=pools)
+    o2, l2 = run_decode(big, pools=pools)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
