@@ -104,11 +104,17 @@ def test_empty_batch_is_a_no_op():
 
 # ----------------------------------------------------- invariants on GPU
 
-def test_constant_v_rows_reproduce_the_constant():
-    w = gen.fwd_inputs(2, 4, 512, 512, 64, "bf16", 901, causal=True, scale=0.125)
-    w.v[...] = gen.float_to_bits_exact(np.full(w.v.shape, -1.5, np.float32), "bf16")
+@pytest.mark.parametrize("dtype,p_ulp", [("bf16", 2.0 ** -9), ("f16", 2.0 ** -11)])
+def test_constant_v_rows_reproduce_the_constant(dtype, p_ulp):
+    """O = sum(p~ v) / sum(p) with p~ the 16-bit-rounded probabilities that
+    feed the MFMA and l summed in fp32: for constant V = c every row is
+    c * sum(p~)/sum(p), within |c| * (half an ulp of the 16-bit type)."""
+    w = gen.fwd_inputs(2, 4, 512, 512, 64, dtype, 901, causal=True, scale=0.125)
+    w.v[...] = gen.float_to_bits_exact(np.full(w.v.shape, -1.5, np.float32), dtype)
     o, _ = gpu_forward(w)
-    assert np.max(np.abs(o + 1.5)) <= 1e-5
+    assert np.max(np.abs(o + 1.5)) <= 1.5 * p_ulp * (1 + 1e-3)
+    # rows whose only key is the diagonal one (row 0) see p = 1 exactly
+    assert np.all(o[:, :, 0] == -1.5)
 
 
 def test_causal_row0_equals_v0_and_zero_q_is_mean():
