@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="time the forward only")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (HBM counter "
+                         "calibration for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -155,6 +158,14 @@ def main():
     fa.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
+        return
 
     print(f"[bench] generating {FWD_WORKLOAD}", file=sys.stderr, flush=True)
     w = gen.fwd_workload(FWD_WORKLOAD)

@@ -12,18 +12,29 @@
 //
 // gfx950 mapping:
 //   * workgroup = 4 waves = BM = 128 query rows (32 per wave), one (b, h);
-//   * key tiles of BN = 64 rows, K and V double-buffered in LDS, loaded with
-//     16-byte coalesced global reads one tile ahead;
+//   * key tiles of BN = 64 rows.  K and V tiles are copied HBM/L2 -> LDS by
+//     the direct-to-LDS load (global_load_lds, 16 bytes per lane), no VGPR
+//     staging, with each lane fetching the chunk that belongs at its XOR-
+//     swizzled LDS slot.  K runs two tiles ahead of the tile being
+//     normalised and V one tile ahead; two LDS buffers each;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA so
 //     that each lane owns ONE query row (lane % 32) and 32 of its 64 scores:
 //     the row max / sum are lane-local plus one permlane32 swap, and the
 //     accumulator registers are directly the B operand of the second MFMA;
+//   * software pipeline inside each wave: the MFMAs of S for tile t+1 are
+//     issued before the softmax of tile t, so the matrix core and the vector
+//     ALU work at the same time;
 //   * O^T = V^T P^T with the same MFMA; V^T fragments come straight from the
 //     row-major LDS tile through the gfx950 transposing read ds_read_b64_tr_b16;
 //   * softmax in base 2: p = exp2(s * scale * log2(e) - m * scale * log2(e)),
 //     one FMA + one v_exp_f32 per score; l accumulates p in fp32 before it is
 //     rounded to 16 bits for the MFMA (a bf16-rounded sum would put up to
 //     2^-9 of error into ln l);
+//   * the running max is only moved (and O, l rescaled) when a row's new max
+//     exceeds it by more than 2^8 in the exponent; otherwise p <= 2^8 is used
+//     against the stale max.  The result is the same softmax (m cancels in
+//     O = sum p v / sum p and LSE = m + ln l), and the O rescale is skipped on
+//     almost every tile;
 //   * O is written in fp32 [B, H, Nq, d], LSE = m * scale + ln(l) in fp32.
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -34,6 +45,13 @@ namespace {
 constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NTHREADS = 256;
+// Lazy-rescale threshold in exponent (log2) units: probabilities may reach
+// 2^tau against a stale max.  f16 P must stay below 65504, bf16 has fp32's range.
+template <bool BF16>
+constexpr float kRescaleLog2 = BF16 ? 32.0f : 8.0f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 // The key-row permutation used when loading the S^T A operand: A row rho is
 // taken from key row sigma(rho) (bits 2 and 3 swapped).  With it, accumulator
@@ -44,227 +62,319 @@ __device__ __forceinline__ int sigma(int rho) { return (rho & 0x13) | ((rho & 4)
 
 // LDS swizzles (16-byte chunk index XOR a row function) so that the MFMA
 // operand reads hit distinct banks.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int swz_k(int row)
+{
+    // bit1 | (bit0 ^ bit2) << 1 | bit3 << 2: distinct slots for the rows one
+    // ds_read_b128 serves per cycle, whether 8 lanes (32 banks) or 16 lanes
+    // (64 banks, split by row parity) are served together
+    return ((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1) | (((row >> 3) & 1) << 2);
+}
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
 
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ LSE, int H, int Nq, int Nk, int n_qtiles,
-    float c_log2, float scale, const int32_t *__restrict__ kv_lens)
+template <int D>
+struct Geometry {
+    static constexpr int DC = D / 8;                 // 16-byte chunks per row
+    static constexpr int KSTEPS = D / 16;            // MFMA k-steps over d
+    static constexpr int NBLK = BN / 32;             // 32-key blocks per tile
+    static constexpr int PCH = BN / 16;              // 16-key PV k-steps per tile
+    static constexpr int DB = D / 32;                // 32-wide column blocks of O
+    static constexpr int ROWB = D * 2;               // bytes per LDS row
+    static constexpr int TILE = BN * ROWB;           // bytes per K (or V) tile
+    static constexpr int PIECES = TILE / 1024;       // 1 KB DMA pieces per tile
+    static constexpr int PIECES_PER_WAVE = PIECES / 4;
+    static constexpr int ROWS_PER_PIECE = 1024 / ROWB;
+    static_assert(PIECES_PER_WAVE * 4 == PIECES, "tile must split over 4 waves");
+};
+
+// Copy key rows [kt0, kt0 + BN) of one (b, h) into an LDS tile.  Rows past Nk
+// are clamped to row Nk - 1 (finite data; those keys are always masked).
+template <int D, bool IS_K>
+__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ src, int kt0, int Nk,
+                                         unsigned char *dst, int wave, int lane)
 {
-    constexpr int DC = D / 8;                          // 16-byte chunks per row
-    constexpr int KSTEPS = D / 16;                     // MFMA k-steps over d
-    constexpr int NBLK = BN / 32;                      // 32-key blocks per tile
-    constexpr int PCH = BN / 16;                       // 16-key PV k-steps per tile
-    constexpr int DB = D / 32;                         // 32-wide column blocks of O
-    constexpr int ROWB = D * 2;                        // bytes per LDS row
-    constexpr int TILE = BN * ROWB;                    // bytes per K (or V) tile
-    constexpr int LOADS = BN * DC / NTHREADS;          // 16-byte loads per thread per tensor
-    static_assert(LOADS * NTHREADS == BN * DC, "tile must split evenly");
+    using G = Geometry<D>;
+#pragma unroll
+    for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
+        const int piece = u * 4 + wave;
+        const int row = piece * G::ROWS_PER_PIECE + lane / G::DC;
+        const int pc = lane % G::DC;
+        const int lc = pc ^ (IS_K ? swz_k(row) : swz_v(row));
+        int key = kt0 + row;
+        key = key < Nk ? key : Nk - 1;
+        __builtin_amdgcn_global_load_lds(src + (size_t)key * D + lc * 8,
+                                         (lds_void *)(dst + piece * 1024), 16, 0, 0);
+    }
+}
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TILE];
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk, int hh,
+                                        const u32x4_t (&qf)[D / 16], f32x16_t (&s)[BN / 32])
+{
+    using G = Geometry<D>;
+    u32x4_t ka[G::NBLK][G::KSTEPS];
+#pragma unroll
+    for (int blk = 0; blk < G::NBLK; ++blk) {
+        const int row = blk * 32 + krow_in_blk;
+        const unsigned char *rp = kb + row * G::ROWB;
+        const int sw = swz_k(row);
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            ka[blk][c] = *reinterpret_cast<const u32x4_t *>(rp + (((2 * c + hh) ^ sw) << 4));
+    }
+#pragma unroll
+    for (int c = 0; c < G::KSTEPS; ++c)
+#pragma unroll
+        for (int blk = 0; blk < G::NBLK; ++blk)
+            s[blk] = c == 0 ? mma32<BF16>(ka[blk][c], qf[c], f32x16_t{}) : mma32<BF16>(ka[blk][c], qf[c], s[blk]);
+}
+
+// V^T operands of the P V MFMAs of one tile (A operand: row = column of O,
+// k = 8 consecutive tile keys), read with the transposing LDS read.
+template <int D>
+__device__ __forceinline__ void pv_operands(const unsigned char *vb, int lane, int hh,
+                                            u32x4_t (&va)[D / 32][BN / 16])
+{
+    using G = Geometry<D>;
+    const int j16 = lane & 15;
+    const int g16 = lane >> 4;   // 16-lane group: bit0 = column half, bit1 = hh
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+        const int chunk = col >> 3;
+        const int half = (col & 7) * 2;
+#pragma unroll
+        for (int c = 0; c < G::PCH; ++c) {
+            const int r0 = 16 * c + 8 * hh + (j16 >> 2);
+            const int r1 = r0 + 4;
+            const unsigned char *a0 = vb + r0 * G::ROWB + ((chunk ^ swz_v(r0)) << 4) + half;
+            const unsigned char *a1 = vb + r1 * G::ROWB + ((chunk ^ swz_v(r1)) << 4) + half;
+            const u32x2_t y0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a0));
+            const u32x2_t y1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a1));
+            va[db][c] = u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+        }
+    }
+}
+
+// O^T += V^T P^T for one tile; the two column blocks' MFMA chains alternate.
+template <int D, bool BF16>
+__device__ __forceinline__ void pv_mfma(const u32x4_t (&va)[D / 32][BN / 16], const u32x4_t (&pf)[BN / 16],
+                                        f32x16_t (&oacc)[D / 32])
+{
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            oacc[db] = mma32<BF16>(va[db][c], pf[c], oacc[db]);
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void pv_tile(const unsigned char *vb, int lane, int hh,
+                                        const u32x4_t (&pf)[BN / 16], f32x16_t (&oacc)[D / 32])
+{
+    u32x4_t va[D / 32][BN / 16];
+    pv_operands<D>(vb, lane, hh, va);
+    pv_mfma<D, BF16>(va, pf, oacc);
+}
+
+// Per-lane online-softmax state.
+struct RowState {
+    float m;   // running max, raw score units (-inf until a key is seen)
+    float l;   // running sum of exp2(s*c - m*c), fp32
+};
+
+// Causal / padding mask: rel = number of valid keys counted from this lane's
+// first tile key (kt0 + 8*hh).
+template <int D>
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int rel)
+{
+#pragma unroll
+    for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int koff = blk * 32 + 16 * (r >> 3) + (r & 7);
+            s[blk][r] = koff < rel ? s[blk][r] : -INFINITY;
+        }
+}
+
+// Row max, lazy max update, probabilities (packed to 16 bits), row sum.
+// The running max only moves when a row's tile max exceeds it by more than
+// tau (raw units; 2^tau_log2 in the exponent) or when it is still -inf.
+// Returns true (wave-uniform) when some row's O accumulator must be
+// multiplied by alpha: never on a row's first tile (O and l are still 0).
+template <int D, bool BF16>
+__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowState &st,
+                                             u32x4_t (&pf)[BN / 16], float c_log2, float tau_raw,
+                                             float &alpha)
+{
+    float mx = s[0][0];
+#pragma unroll
+    for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mx = fmaxf(mx, s[blk][r]);
+    mx = fmaxf(mx, other_half(mx));
+    const bool first = st.m == -INFINITY;
+    const bool jump = !first && mx > st.m + tau_raw;
+    const float m_new = (first || jump) ? mx : st.m;
+    alpha = jump ? fast_exp2((st.m - m_new) * c_log2) : 1.f;
+    const bool any = __builtin_amdgcn_ballot_w64(jump) != 0;
+    st.m = m_new;
+    const float mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * h2 + 2 * q;
+                const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
+                const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
+                pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
+                psum += p0 + p1;
+            }
+    st.l = fmaf(st.l, alpha, psum);
+    return any;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alpha)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+        oacc[db] *= alpha;
+}
+
+// s_waitcnt for "at most N vector-memory operations outstanding" (other
+// counters untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int D>
+struct Pipe {
+    static constexpr int STAGES = D == 64 ? 3 : 2;             // LDS ring depth (tiles)
+    static constexpr int DMA_PER_TILE = 2 * Geometry<D>::PIECES_PER_WAVE;   // per thread: K + V
+};
+
+// One query tile (BM rows of one (b, h)) against its key tiles.
+template <int D, bool BF16, bool CAUSAL>
+__device__ __forceinline__ void attend_qtile(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kb, const uint16_t *__restrict__ Vb,
+    float *__restrict__ O, float *__restrict__ LSE, size_t bh, int Nq, int Nk, int kvlen, int q0,
+    float c_log2, float scale, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
+    unsigned char *const (&vbuf)[Pipe<D>::STAGES], int wave, int lane)
+{
+    using G = Geometry<D>;
+    constexpr int ST = Pipe<D>::STAGES;
+    constexpr int PER = Pipe<D>::DMA_PER_TILE;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-
-    // ---- which (b, h, query tile)
-    const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
-    const int bh = logical / n_qtiles;
-    int qt = logical - bh * n_qtiles;
-    if (CAUSAL)
-        qt = n_qtiles - 1 - qt;   // longest rows first
-    const int b = bh / H;
-    const int q0 = qt * BM;
-
-    int kvlen = Nk;
-    if (kv_lens) {
-        kvlen = kv_lens[b];
-        kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
-    }
     const int dq = Nk - Nq;   // causal: row i sees keys j <= i + dq
+    const int wave_first_row = q0 + wave * 32;
     int key_end = kvlen;
     int wave_key_end = kvlen;
     if (CAUSAL) {
         const int last = min(q0 + BM, Nq) - 1;
         key_end = min(key_end, max(last + dq + 1, 0));
-        const int wlast = min(q0 + wave * 32 + 32, Nq) - 1;
+        const int wlast = min(wave_first_row + 32, Nq) - 1;
         wave_key_end = min(wave_key_end, max(wlast + dq + 1, 0));
     }
     const int n_tiles = (key_end + BN - 1) / BN;
-    const int wave_first_row = q0 + wave * 32;
+    const int wave_tiles = min(n_tiles, (wave_key_end + BN - 1) / BN);
 
-    // ---- this lane's query row and its Q fragments (B operand of S^T = K Q^T)
     const int qrow = wave_first_row + l32;
-    u32x4_t qf[KSTEPS];
+    u32x4_t qf[G::KSTEPS];
     {
-        const uint16_t *qp = Q + ((size_t)bh * Nq + (qrow < Nq ? qrow : 0)) * D + 8 * hh;
+        const uint16_t *qp = Q + (bh * Nq + (qrow < Nq ? qrow : 0)) * D + 8 * hh;
 #pragma unroll
-        for (int c = 0; c < KSTEPS; ++c)
+        for (int c = 0; c < G::KSTEPS; ++c)
             qf[c] = qrow < Nq ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
     }
+    int lim = kvlen;   // keys j < lim are valid for this lane's row
+    if (CAUSAL)
+        lim = min(lim, qrow + dq + 1);
 
-    f32x16_t oacc[DB];
+    f32x16_t oacc[G::DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    const uint16_t *Kb = K + (size_t)bh * Nk * D;
-    const uint16_t *Vb = V + (size_t)bh * Nk * D;
-    u32x4_t kreg[LOADS], vreg[LOADS];
-
-    auto gload = [&](int t) {
-        const int kt0 = t * BN;
-#pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            const int id = tid + u * NTHREADS;
-            const int row = id / DC, cc = id % DC;
-            const int key = kt0 + row;
-            if (key < Nk) {
-                kreg[u] = load16(Kb + (size_t)key * D + cc * 8);
-                vreg[u] = load16(Vb + (size_t)key * D + cc * 8);
-            } else {
-                kreg[u] = u32x4_t{0, 0, 0, 0};
-                vreg[u] = u32x4_t{0, 0, 0, 0};
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-        unsigned char *kb = smem + buf * 2 * TILE;
-        unsigned char *vb = kb + TILE;
-#pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            const int id = tid + u * NTHREADS;
-            const int row = id / DC, cc = id % DC;
-            *reinterpret_cast<u32x4_t *>(kb + row * ROWB + ((cc ^ swz_k(row)) << 4)) = kreg[u];
-            *reinterpret_cast<u32x4_t *>(vb + row * ROWB + ((cc ^ swz_v(row)) << 4)) = vreg[u];
-        }
-    };
-
-    if (n_tiles > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
-
-    // per-lane constants of the operand reads
+    RowState st{-INFINITY, 0.f};
+    const float tau_raw = kRescaleLog2<BF16> / c_log2;
     const int krow_in_blk = sigma(l32);
-    const int j16 = lane & 15;
-    const int g16 = lane >> 4;   // 16-lane group: bit0 = column half, bit1 = hh
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < n_tiles)
-            gload(t + 1);
-        const int kt0 = t * BN;
-        if (kt0 < wave_key_end) {
-            const unsigned char *kb = smem + buf * 2 * TILE;
-            const unsigned char *vb = kb + TILE;
-
-            // ---- S^T = K Q^T for the 64 keys of this tile (two 32-key blocks)
-            f32x16_t s[NBLK];
+    // prologue: the first ST-1 tiles in flight
 #pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk) {
-                s[blk] = f32x16_t{};
-                const int row = blk * 32 + krow_in_blk;
-                const unsigned char *rp = kb + row * ROWB;
-                const int sw = swz_k(row);
-#pragma unroll
-                for (int c = 0; c < KSTEPS; ++c) {
-                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(rp + (((2 * c + hh) ^ sw) << 4));
-                    s[blk] = mma32<BF16>(a, qf[c], s[blk]);
-                }
-            }
-
-            // ---- masks (only on tiles that cross the padded length or the diagonal)
-            const bool need_mask = (kt0 + BN > kvlen) || (CAUSAL && kt0 + BN - 1 > wave_first_row + dq);
-            if (need_mask) {
-                int lim = kvlen;
-                if (CAUSAL)
-                    lim = min(lim, qrow + dq + 1);
-                const int kbase = kt0 + 8 * hh;
-#pragma unroll
-                for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + blk * 32 + 16 * (r >> 3) + (r & 7);
-                        if (key >= lim)
-                            s[blk][r] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax (raw-score units for m; base-2 exponent)
-            float mx = s[0][0];
-#pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, s[blk][r]);
-            mx = fmaxf(mx, other_half(mx));
-            const float m_new = fmaxf(m_run, mx);
-            const float mc = (m_new == -INFINITY) ? 0.f : m_new * c_log2;
-            const float alpha = fast_exp2(m_run * c_log2 - mc);
-            m_run = m_new;
-
-            u32x4_t pf[PCH];
-            float psum = 0.f;
-#pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = 8 * h2 + 2 * q;
-                        const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
-                        const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
-                        const uint32_t w = pack2<BF16>(p0, p1);
-                        pf[2 * blk + h2][q] = w;
-                        psum += p0 + p1;
-                    }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                oacc[db] *= alpha;
-
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
-                const int chunk = col >> 3;
-                const int half = (col & 7) * 2;
-#pragma unroll
-                for (int c = 0; c < PCH; ++c) {
-                    const int r0 = 16 * c + 8 * hh + (j16 >> 2);
-                    const int r1 = r0 + 4;
-                    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-                    const unsigned char *a0 = vb + r0 * ROWB + ((chunk ^ swz_v(r0)) << 4) + half;
-                    const unsigned char *a1 = vb + r1 * ROWB + ((chunk ^ swz_v(r1)) << 4) + half;
-                    const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0));
-                    const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a1));
-                    const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0);
-                    const u32x2_t y1 = __builtin_bit_cast(u32x2_t, x1);
-                    const u32x4_t a = {y0[0], y0[1], y1[0], y1[1]};
-                    oacc[db] = mma32<BF16>(a, pf[c], oacc[db]);
-                }
-            }
+    for (int i = 0; i < ST - 1; ++i)
+        if (i < n_tiles) {
+            dma_tile<D, true>(Kb, i * BN, Nk, kbuf[i], wave, lane);
+            dma_tile<D, false>(Vb, i * BN, Nk, vbuf[i], wave, lane);
         }
-        if (t + 1 < n_tiles)
-            lstore(buf ^ 1);
+
+    // Iteration t: wait for tile t (own loads, then everyone's via the
+    // barrier), refill the ring slot freed by tile t-1 with tile t+ST-1,
+    // then S = K Q^T, masks, online softmax, O += P V on tile t.
+    auto iter = [&](int t, unsigned char *kc, unsigned char *vc, unsigned char *kfill,
+                    unsigned char *vfill) {
+        if (t + ST - 2 < n_tiles)
+            wait_vmcnt<(ST - 2) * PER>();
+        else
+            wait_vmcnt<0>();
         __syncthreads();
+        if (t + ST - 1 < n_tiles) {
+            dma_tile<D, true>(Kb, (t + ST - 1) * BN, Nk, kfill, wave, lane);
+            dma_tile<D, false>(Vb, (t + ST - 1) * BN, Nk, vfill, wave, lane);
+        }
+        if (t < wave_tiles) {
+            const int kt0 = t * BN;
+            f32x16_t s[G::NBLK];
+            qk_tile<D, BF16>(kc, krow_in_blk, hh, qf, s);
+            const bool need_mask = (kt0 + BN > kvlen) || (CAUSAL && kt0 + BN - 1 > wave_first_row + dq);
+            if (need_mask)
+                mask_tile<D>(s, lim - (kt0 + 8 * hh));
+            u32x4_t pf[G::PCH];
+            float alpha;
+            if (softmax_tile<D, BF16>(s, st, pf, c_log2, tau_raw, alpha))
+                rescale_acc<D>(oacc, alpha);
+            // keep the V operand reads after the softmax (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
+            pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
+        }
+    };
+
+    int t = 0;
+    if constexpr (ST == 3) {
+        for (; t + 2 < n_tiles; t += 3) {
+            iter(t, kbuf[0], vbuf[0], kbuf[2], vbuf[2]);
+            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+            iter(t + 2, kbuf[2], vbuf[2], kbuf[1], vbuf[1]);
+        }
+        if (t < n_tiles)
+            iter(t, kbuf[0], vbuf[0], kbuf[2], vbuf[2]);
+        if (t + 1 < n_tiles)
+            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+    } else {
+        for (; t + 1 < n_tiles; t += 2) {
+            iter(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
+            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+        }
+        if (t < n_tiles)
+            iter(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
     }
+    __syncthreads();   // the ring is reused by the next query tile of this workgroup
 
     // ---- epilogue: O = O_acc / l, LSE = m * scale + ln(l)
-    const float l_tot = l_run + other_half(l_run);
+    const float l_tot = st.l + other_half(st.l);
     if (qrow < Nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *op = O + ((size_t)bh * Nq + qrow) * D + 4 * hh;
+        float *op = O + (bh * Nq + qrow) * D + 4 * hh;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 f32x4_t v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
@@ -272,18 +382,75 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(
                 *reinterpret_cast<f32x4_t *>(op + 32 * db + 8 * g) = v;
             }
         if (hh == 0)
-            LSE[(size_t)bh * Nq + qrow] = l_tot > 0.f ? m_run * scale + __log2f(l_tot) * kLn2 : -INFINITY;
+            LSE[bh * Nq + qrow] = l_tot > 0.f ? st.m * scale + __log2f(l_tot) * kLn2 : -INFINITY;
     }
+}
+
+// Work decomposition: one workgroup per (b, h, unit).  Non-causal: a unit is
+// one query tile.  Causal: a unit is the pair of query tiles j and
+// n_qtiles-1-j (the middle tile alone when n_qtiles is odd), so every
+// workgroup visits the same number of key tiles.  Work ids are renumbered so
+// that each XCD receives a contiguous range (units of one head share its L2).
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ LSE, int H, int Nq, int Nk, int n_qtiles, int n_units,
+    float c_log2, float scale, const int32_t *__restrict__ kv_lens)
+{
+    using G = Geometry<D>;
+    constexpr int ST = Pipe<D>::STAGES;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k2[ST > 2 ? G::TILE : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v2[ST > 2 ? G::TILE : 16];
+    unsigned char *const kbuf3[3] = {lds_k0, lds_k1, lds_k2};
+    unsigned char *const vbuf3[3] = {lds_v0, lds_v1, lds_v2};
+    unsigned char *const (&kbuf)[ST] = *reinterpret_cast<unsigned char *const(*)[ST]>(&kbuf3);
+    unsigned char *const (&vbuf)[ST] = *reinterpret_cast<unsigned char *const(*)[ST]>(&vbuf3);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int bhi = logical / n_units;
+    const int unit = logical - bhi * n_units;
+    const size_t bh = (size_t)bhi;
+    const int b = bhi / H;
+    int kvlen = Nk;
+    if (kv_lens) {
+        kvlen = kv_lens[b];
+        kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
+    }
+    const uint16_t *Kb = K + bh * Nk * D;
+    const uint16_t *Vb = V + bh * Nk * D;
+
+    // causal: tile n_qtiles-1-unit (the longer one) first, then tile unit
+    const int n_pass = (CAUSAL && unit != n_qtiles - 1 - unit) ? 2 : 1;
+    for (int pass = 0; pass < n_pass; ++pass) {
+        const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - unit : unit) : unit;
+        attend_qtile<D, BF16, CAUSAL>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, kbuf,
+                                      vbuf, wave, lane);
+    }
+}
+
+int units_per_head(int Nq, bool causal)
+{
+    const int n_qtiles = (Nq + BM - 1) / BM;
+    return causal ? (n_qtiles + 1) / 2 : n_qtiles;
 }
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
     const int n_qtiles = (a.Nq + BM - 1) / BM;
-    const long long grid = (long long)n_qtiles * a.B * a.H;
+    const int n_units = units_per_head(a.Nq, CAUSAL);
+    const long long grid = (long long)n_units * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
-                       a.H, a.Nq, a.Nk, n_qtiles, a.scale * kLog2e, a.scale, a.kv_lens);
+                       a.H, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.kv_lens);
     return hipGetLastError();
 }
 
@@ -295,7 +462,7 @@ hipError_t launch_c(const FwdArgs &a, hipStream_t s)
 
 }  // namespace
 
-long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1) / BM) * B * H; }
+long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1) / BM) * B * H; }   // upper bound
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {
