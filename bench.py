@@ -42,7 +42,7 @@ DEC_WORKLOAD = "decode_paged_s32h32_d128_bf16"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_causal_b8h16_n4096_d64.json")
-FWD_SOURCE = os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", "fa_fwd.hip")
+DEC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_paged_s32h32_d128.json")
 
 
 def attention_flops(B, H, Nq, Nk, d, causal):
@@ -70,25 +70,71 @@ def fwd_bytes(B, H, Nq, Nk, d, elem=2):
     return B * H * (Nq + 2 * Nk) * d * elem + B * H * Nq * d * 4 + B * H * Nq * 4
 
 
-def kernel_digest():
+def kernel_digest(sources=("fa_fwd.hip", "fa_common.h")):
     h = hashlib.sha256()
-    for name in ("fa_fwd.hip", "fa_common.h"):
+    for name in sources:
         with open(os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per forward launch from the committed rocprofv3 counter runs,
-    or None if they were taken on a different version of the kernel."""
+DEC_SOURCES = ("fa_decode.hip", "fa_common.h")
+
+
+def measured_traffic(path=TRAFFIC_FILE, sources=("fa_fwd.hip", "fa_common.h")):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    if they were taken on a different version of the kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_digest") != kernel_digest():
+    if t.get("kernel_digest") != kernel_digest(sources):
         return None
     return t.get("bytes_per_launch")
+
+
+def _counter_means(csv_path, counter):
+    import csv
+    import collections
+
+    vals = collections.defaultdict(list)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def record_traffic(d, copy_bytes):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
+    this benchmark and of a plain copy of copy_bytes into bytes per launch:
+    each counter is scaled by (bytes the copy moves) / (what it reads for the
+    copy).  Expects run dirs <d>/{fwd,copy}_{FETCH_SIZE,WRITE_SIZE}/ holding
+    run_counter_collection.csv (see the profile notes for the commands)."""
+    def one(sub, counter):
+        return _counter_means(os.path.join(d, sub, "run_counter_collection.csv"), counter)
+
+    factor = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v for k, v in one("copy_" + c, c).items() if "copyBuffer" in k]
+        factor[c] = copy_bytes / (copy[0] * 1024.0)
+    out = {}
+    for label, match, path, sources in (
+            ("fwd", "fwd_kernel", TRAFFIC_FILE, ("fa_fwd.hip", "fa_common.h")),
+            ("decode", "decode_", DEC_TRAFFIC_FILE, DEC_SOURCES)):
+        rec = {"kernel_digest": kernel_digest(sources), "calibration": factor}
+        total = 0.0
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib = sum(v for k, v in one("fwd_" + c, c).items() if match in k)
+            rec[c + "_KiB_raw"] = kib
+            rec[c + "_bytes"] = kib * 1024.0 * factor[c]
+            total += rec[c + "_bytes"]
+        rec["bytes_per_launch"] = total
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        out[label] = rec
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
@@ -114,8 +160,19 @@ def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
 
     rows, o_ref, lse_ref, dt, flops = run(256 * cores)
     if dt < target_s:
-        want = int(len(rows) * min(target_s / max(dt, 1e-3), 64.0))
-        rows, o_ref, lse_ref, dt, flops = run(min(want, B * H * Nq))
+        want = int(len(rows) * target_s / max(dt, 1e-3))
+        if want >= B * H * Nq:
+            # the whole workload fits the time budget: every row, in order
+            rows = np.arange(B * H * Nq, dtype=np.int64)
+            t0 = time.perf_counter()
+            o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal,
+                                                  w.kv_lens, rows=rows, nthreads=cores)
+            dt = time.perf_counter() - t0
+            i = rows % Nq
+            n_valid = np.minimum(i + 1, Nk) if w.causal else np.full(rows.shape, Nk)
+            flops = float(np.sum(4.0 * d * n_valid))
+        else:
+            rows, o_ref, lse_ref, dt, flops = run(want)
     og = o_gpu.reshape(-1, d)[rows].astype(np.float64)
     lg = lse_gpu.reshape(-1)[rows].astype(np.float64)
     err = np.abs(og - o_ref)
@@ -124,8 +181,9 @@ def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{len(rows)} uniformly drawn query rows of {B * H * Nq} "
-                  f"({FWD_WORKLOAD}), fp64, {dt:.1f} s",
+        "sample": (f"all {B * H * Nq} query rows" if len(rows) == B * H * Nq else
+                   f"{len(rows)} uniformly drawn query rows of {B * H * Nq}")
+                  + f" ({FWD_WORKLOAD}), fp64, {dt:.1f} s",
         "seconds": dt,
         "sample_parity": {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
                           "lse_rel": float(np.max(np.abs(lg - lse_ref) /
@@ -144,7 +202,13 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter "
                          "calibration for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write the profiles/traffic_*.json files from rocprofv3 counter "
+                         "runs in DIR (CPU only) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.copy_bytes or (1 << 30))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by batch/head with no communication; see the design notes)",
@@ -249,7 +313,8 @@ def main():
             "kernel_ms_p90": float(np.percentile(dec_ms, 90)),
             "bytes": dbytes, "tokens": int(dec.kv_lens.sum()),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(DEC_TRAFFIC_FILE, DEC_SOURCES)},
         }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

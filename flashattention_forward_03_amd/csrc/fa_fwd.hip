@@ -208,12 +208,18 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
                                              u32x4_t (&pf)[BN / 16], float c_log2, float tau_raw,
                                              float &alpha)
 {
-    float mx = s[0][0];
+    // row max over this lane's 32 scores as 4 independent max3 chains (ILP)
+    float mxp[4];
 #pragma unroll
-    for (int blk = 0; blk < BN / 32; ++blk)
+    for (int k = 0; k < 4; ++k) {
+        const int blk = k >> 1, r0 = (k & 1) * 8;
+        float m = fmaxf(s[blk][r0], s[blk][r0 + 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            mx = fmaxf(mx, s[blk][r]);
+        for (int r = 2; r < 8; r += 2)
+            m = fmaxf(m, fmaxf(s[blk][r0 + r], s[blk][r0 + r + 1]));
+        mxp[k] = m;
+    }
+    float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
     mx = fmaxf(mx, other_half(mx));
     const bool first = st.m == -INFINITY;
     const bool jump = !first && mx > st.m + tau_raw;
@@ -222,7 +228,8 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
     const bool any = __builtin_amdgcn_ballot_w64(jump) != 0;
     st.m = m_new;
     const float mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
-    float psum = 0.f;
+    // probabilities; the row sum in 4 independent partial sums (ILP)
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < BN / 32; ++blk)
 #pragma unroll
@@ -233,9 +240,9 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
                 const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
                 const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
                 pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
-                psum += p0 + p1;
+                ps[q] += p0 + p1;
             }
-    st.l = fmaf(st.l, alpha, psum);
+    st.l = fmaf(st.l, alpha, (ps[0] + ps[1]) + (ps[2] + ps[3]));
     return any;
 }
 
@@ -263,11 +270,11 @@ struct Pipe {
 };
 
 // One query tile (BM rows of one (b, h)) against its key tiles.
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16>
 __device__ __forceinline__ void attend_qtile(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kb, const uint16_t *__restrict__ Vb,
     float *__restrict__ O, float *__restrict__ LSE, size_t bh, int Nq, int Nk, int kvlen, int q0,
-    float c_log2, float scale, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
+    float c_log2, float scale, bool causal, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
     unsigned char *const (&vbuf)[Pipe<D>::STAGES], int wave, int lane)
 {
     using G = Geometry<D>;
@@ -279,7 +286,7 @@ __device__ __forceinline__ void attend_qtile(
     const int wave_first_row = q0 + wave * 32;
     int key_end = kvlen;
     int wave_key_end = kvlen;
-    if (CAUSAL) {
+    if (causal) {
         const int last = min(q0 + BM, Nq) - 1;
         key_end = min(key_end, max(last + dq + 1, 0));
         const int wlast = min(wave_first_row + 32, Nq) - 1;
@@ -297,7 +304,7 @@ __device__ __forceinline__ void attend_qtile(
             qf[c] = qrow < Nq ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
     }
     int lim = kvlen;   // keys j < lim are valid for this lane's row
-    if (CAUSAL)
+    if (causal)
         lim = min(lim, qrow + dq + 1);
 
     f32x16_t oacc[G::DB];
@@ -334,7 +341,8 @@ __device__ __forceinline__ void attend_qtile(
             const int kt0 = t * BN;
             f32x16_t s[G::NBLK];
             qk_tile<D, BF16>(kc, krow_in_blk, hh, qf, s);
-            const bool need_mask = (kt0 + BN > kvlen) || (CAUSAL && kt0 + BN - 1 > wave_first_row + dq);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool need_mask = (kt0 + BN > kvlen) || (causal && kt0 + BN - 1 > wave_first_row + dq);
             if (need_mask)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
@@ -386,16 +394,17 @@ __device__ __forceinline__ void attend_qtile(
     }
 }
 
-// Work decomposition: one workgroup per (b, h, unit).  Non-causal: a unit is
-// one query tile.  Causal: a unit is the pair of query tiles j and
-// n_qtiles-1-j (the middle tile alone when n_qtiles is odd), so every
-// workgroup visits the same number of key tiles.  Work ids are renumbered so
-// that each XCD receives a contiguous range (units of one head share its L2).
-template <int D, bool BF16, bool CAUSAL>
+// Work decomposition: one workgroup per (b, h, unit).  Causal: a unit is the
+// pair of query tiles j and n_qtiles-1-j (the middle tile alone when
+// n_qtiles is odd), so every workgroup visits the same number of key tiles.
+// Non-causal: a unit is one query tile.  Work ids are renumbered so that
+// each XCD receives a contiguous range (units of one head share its L2).
+// The causal flag is a runtime argument: both modes share one code path.
+template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     float *__restrict__ O, float *__restrict__ LSE, int H, int Nq, int Nk, int n_qtiles, int n_units,
-    float c_log2, float scale, const int32_t *__restrict__ kv_lens)
+    float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
     constexpr int ST = Pipe<D>::STAGES;
@@ -413,6 +422,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool causal = causal_flag != 0;
 
     const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int bhi = logical / n_units;
@@ -428,11 +438,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const uint16_t *Vb = V + bh * Nk * D;
 
     // causal: tile n_qtiles-1-unit (the longer one) first, then tile unit
-    const int n_pass = (CAUSAL && unit != n_qtiles - 1 - unit) ? 2 : 1;
+    const int n_pass = (causal && unit != n_qtiles - 1 - unit) ? 2 : 1;
     for (int pass = 0; pass < n_pass; ++pass) {
-        const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - unit : unit) : unit;
-        attend_qtile<D, BF16, CAUSAL>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, kbuf,
-                                      vbuf, wave, lane);
+        const int qt = causal ? (pass == 0 ? n_qtiles - 1 - unit : unit) : unit;
+        attend_qtile<D, BF16>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal, kbuf,
+                              vbuf, wave, lane);
     }
 }
 
@@ -442,22 +452,17 @@ int units_per_head(int Nq, bool causal)
     return causal ? (n_qtiles + 1) / 2 : n_qtiles;
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
     const int n_qtiles = (a.Nq + BM - 1) / BM;
-    const int n_units = units_per_head(a.Nq, CAUSAL);
+    const int n_units = units_per_head(a.Nq, a.causal);
     const long long grid = (long long)n_units * a.B * a.H;
-    hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
-                       a.H, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.kv_lens);
+                       a.H, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.causal ? 1 : 0,
+                       a.kv_lens);
     return hipGetLastError();
-}
-
-template <int D, bool BF16>
-hipError_t launch_c(const FwdArgs &a, hipStream_t s)
-{
-    return a.causal ? launch<D, BF16, true>(a, s) : launch<D, BF16, false>(a, s);
 }
 
 }  // namespace
@@ -467,8 +472,8 @@ long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1)
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {
     if (a.d == 64)
-        return a.bf16 ? launch_c<64, true>(a, stream) : launch_c<64, false>(a, stream);
-    return a.bf16 ? launch_c<128, true>(a, stream) : launch_c<128, false>(a, stream);
+        return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }
 
 }  // namespace fa
