@@ -45,10 +45,10 @@ namespace {
 constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NTHREADS = 256;
-// Lazy-rescale threshold in exponent (log2) units: probabilities may reach
-// 2^tau against a stale max.  f16 P must stay below 65504, bf16 has fp32's range.
+// Bound on the probabilities formed against a stale running max, in
+// exponent (log2) units: f16 P must stay below 65504, bf16 has fp32's range.
 template <bool BF16>
-constexpr float kRescaleLog2 = BF16 ? 32.0f : 8.0f;
+constexpr float kRescaleLog2 = BF16 ? 32.0f : 15.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -198,37 +198,13 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int rel)
         }
 }
 
-// Row max, lazy max update, probabilities (packed to 16 bits), row sum.
-// The running max only moves when a row's tile max exceeds it by more than
-// tau (raw units; 2^tau_log2 in the exponent) or when it is still -inf.
-// Returns true (wave-uniform) when some row's O accumulator must be
-// multiplied by alpha: never on a row's first tile (O and l are still 0).
-template <int D, bool BF16>
-__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowState &st,
-                                             u32x4_t (&pf)[BN / 16], float c_log2, float tau_raw,
-                                             float &alpha)
+// Probabilities of one tile against the row's current (possibly stale) max
+// m: p = exp2(s*c - m*c), packed to 16 bits for the MFMA, summed in fp32
+// (4 independent partial sums).  Returns the row sum of this lane's 32 p.
+template <bool BF16>
+__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[BN / 32], float mc, float c_log2,
+                                          u32x4_t (&pf)[BN / 16])
 {
-    // row max over this lane's 32 scores as 4 independent max3 chains (ILP)
-    float mxp[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int blk = k >> 1, r0 = (k & 1) * 8;
-        float m = fmaxf(s[blk][r0], s[blk][r0 + 1]);
-#pragma unroll
-        for (int r = 2; r < 8; r += 2)
-            m = fmaxf(m, fmaxf(s[blk][r0 + r], s[blk][r0 + r + 1]));
-        mxp[k] = m;
-    }
-    float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
-    mx = fmaxf(mx, other_half(mx));
-    const bool first = st.m == -INFINITY;
-    const bool jump = !first && mx > st.m + tau_raw;
-    const float m_new = (first || jump) ? mx : st.m;
-    alpha = jump ? fast_exp2((st.m - m_new) * c_log2) : 1.f;
-    const bool any = __builtin_amdgcn_ballot_w64(jump) != 0;
-    st.m = m_new;
-    const float mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
-    // probabilities; the row sum in 4 independent partial sums (ILP)
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < BN / 32; ++blk)
@@ -242,8 +218,52 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
                 pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
                 ps[q] += p0 + p1;
             }
-    st.l = fmaf(st.l, alpha, (ps[0] + ps[1]) + (ps[2] + ps[3]));
-    return any;
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// Online softmax step for one tile.  The running max m only has to keep
+// p = exp2(s*c - m*c) below 2^tau (no overflow in the 16-bit P, fp32 sums),
+// and the exact softmax does not depend on which m is used (m cancels in
+// O = sum p v / sum p and LSE = m + ln l).  So the common path does not
+// compute the tile max at all: it forms p against the current m and checks
+// the row sum (sum >= max p); only when some row of the wave exceeds 2^tau,
+// overflowed, or has no finite m yet (its first keys) does the wave take
+// the exact path: tile max, new m = max(m, tile max), rescale of l and O by
+// alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
+// uniform) when O must be multiplied by alpha (done by the caller).
+template <int D, bool BF16>
+__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowState &st,
+                                             u32x4_t (&pf)[BN / 16], float c_log2, float tau_log2,
+                                             float &alpha)
+{
+    const float limit = exp2f(tau_log2);
+    float mc = st.m == -INFINITY ? 0.f : st.m * c_log2;
+    alpha = 1.f;
+    bool rescale = false;
+    // at most two passes: the second one runs against the exact max (p <= 1)
+    for (int pass = 0; pass < 2; ++pass) {
+        const float psum = exp_tile<BF16>(s, mc, c_log2, pf);
+        const bool bad = pass == 0 && (st.m == -INFINITY || !(psum <= limit));
+        if (__builtin_amdgcn_ballot_w64(bad) == 0) {
+            st.l = fmaf(st.l, alpha, psum);
+            break;
+        }
+        // exact path: tile max (lane-local, then the other half of the wave)
+        float mx = s[0][0];
+#pragma unroll
+        for (int blk = 0; blk < BN / 32; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[blk][r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float m_new = fmaxf(st.m, mx);
+        // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
+        alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
+        st.m = m_new;
+        mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
+        rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+    }
+    return rescale;
 }
 
 template <int D>
@@ -312,7 +332,7 @@ __device__ __forceinline__ void attend_qtile(
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
     RowState st{-INFINITY, 0.f};
-    const float tau_raw = kRescaleLog2<BF16> / c_log2;
+    const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
 
     // prologue: the first ST-1 tiles in flight
@@ -347,7 +367,7 @@ __device__ __forceinline__ void attend_qtile(
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
             float alpha;
-            if (softmax_tile<D, BF16>(s, st, pf, c_log2, tau_raw, alpha))
+            if (softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha))
                 rescale_acc<D>(oacc, alpha);
             // keep the V operand reads after the softmax (register pressure)
             __builtin_amdgcn_sched_barrier(0);
