@@ -81,6 +81,8 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
         return FA_OK;
     if (fa::fwd_grid_size(B, H, Nq) > INT_MAX)
         return FA_ERR_SHAPE;
+    if (((long long)Nk + 64) * d * 2 > INT_MAX)   // per-(b, h) key span: 32-bit buffer offsets
+        return FA_ERR_SHAPE;
     if (!q || !o || !lse || (Nk > 0 && (!k || !v)))
         return FA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||

@@ -12,29 +12,30 @@
 //
 // gfx950 mapping:
 //   * workgroup = 4 waves = BM = 128 query rows (32 per wave), one (b, h);
+//     three workgroups per CU (one wave of each per SIMD);
 //   * key tiles of BN = 64 rows.  K and V tiles are copied HBM/L2 -> LDS by
-//     the direct-to-LDS load (global_load_lds, 16 bytes per lane), no VGPR
-//     staging, with each lane fetching the chunk that belongs at its XOR-
-//     swizzled LDS slot.  K runs two tiles ahead of the tile being
-//     normalised and V one tile ahead; two LDS buffers each;
+//     the buffer-to-LDS load (16 bytes per lane, no VGPR staging); each lane
+//     fetches the chunk that belongs at its XOR-swizzled LDS slot, and rows
+//     past Nk fall outside the buffer range and read as zero.  The LDS ring
+//     holds three K and three V tiles (two for d = 128), filled two tiles
+//     ahead of use;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA so
 //     that each lane owns ONE query row (lane % 32) and 32 of its 64 scores:
-//     the row max / sum are lane-local plus one permlane32 swap, and the
+//     the row sum is lane-local plus one permlane32 swap, and the
 //     accumulator registers are directly the B operand of the second MFMA;
-//   * software pipeline inside each wave: the MFMAs of S for tile t+1 are
-//     issued before the softmax of tile t, so the matrix core and the vector
-//     ALU work at the same time;
 //   * O^T = V^T P^T with the same MFMA; V^T fragments come straight from the
 //     row-major LDS tile through the gfx950 transposing read ds_read_b64_tr_b16;
 //   * softmax in base 2: p = exp2(s * scale * log2(e) - m * scale * log2(e)),
 //     one FMA + one v_exp_f32 per score; l accumulates p in fp32 before it is
 //     rounded to 16 bits for the MFMA (a bf16-rounded sum would put up to
 //     2^-9 of error into ln l);
-//   * the running max is only moved (and O, l rescaled) when a row's new max
-//     exceeds it by more than 2^8 in the exponent; otherwise p <= 2^8 is used
-//     against the stale max.  The result is the same softmax (m cancels in
-//     O = sum p v / sum p and LSE = m + ln l), and the O rescale is skipped on
-//     almost every tile;
+//   * the running max m is moved only when needed: p is formed against the
+//     current m and the row sums are checked; only a tile whose sum exceeds
+//     2^32 (bf16) or 2^15 (f16) in some row, or a row without a finite m yet,
+//     takes the exact update (tile max, rescale of l and O).  The result is
+//     the same softmax, since m cancels in O = sum p v / sum p and in
+//     LSE = m + ln l, and the max and the O rescale are skipped on almost
+//     every tile;
 //   * O is written in fp32 [B, H, Nq, d], LSE = m * scale + ln(l) in fp32.
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -86,11 +87,14 @@ struct Geometry {
     static_assert(PIECES_PER_WAVE * 4 == PIECES, "tile must split over 4 waves");
 };
 
-// Copy key rows [kt0, kt0 + BN) of one (b, h) into an LDS tile.  Rows past Nk
-// are clamped to row Nk - 1 (finite data; those keys are always masked).
+// Copy key rows [kt0, kt0 + BN) of one (b, h) into an LDS tile with the
+// buffer-to-LDS load (16 bytes per lane).  The buffer resource covers the
+// Nk rows of this (b, h); rows past Nk are out of range and read as zero
+// (those keys are always masked).  off[u] is the lane's byte offset for its
+// u-th 1 KB piece of tile 0 (chunk picked so that it lands in its swizzled
+// LDS slot).
 template <int D, bool IS_K>
-__device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ src, int kt0, int Nk,
-                                         unsigned char *dst, int wave, int lane)
+__device__ __forceinline__ void dma_offsets(int wave, int lane, unsigned (&off)[Geometry<D>::PIECES_PER_WAVE])
 {
     using G = Geometry<D>;
 #pragma unroll
@@ -99,14 +103,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t *__restrict__ src, int k
         const int row = piece * G::ROWS_PER_PIECE + lane / G::DC;
         const int pc = lane % G::DC;
         const int lc = pc ^ (IS_K ? swz_k(row) : swz_v(row));
-        int key = kt0 + row;
-        key = key < Nk ? key : Nk - 1;
-        __builtin_amdgcn_global_load_lds(src + (size_t)key * D + lc * 8,
-                                         (lds_void *)(dst + piece * 1024), 16, 0, 0);
+        off[u] = (unsigned)(row * D + lc * 8) * 2u;
     }
 }
 
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t *base, int nbytes, const unsigned *off,
+                                         int kt0, unsigned char *dst, int wave)
+{
+    using G = Geometry<D>;
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists for the GPU target only
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < G::PIECES_PER_WAVE; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(dst + (u * 4 + wave) * 1024), 16,
+                                                 off[u] + (unsigned)kt0 * G::ROWB, 0, 0, 0);
+#endif
+}
 
 template <int D, bool BF16>
 __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk, int hh,
@@ -334,13 +347,17 @@ __device__ __forceinline__ void attend_qtile(
     RowState st{-INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
+    const int kv_bytes = Nk * G::ROWB;
+    unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, koff);
+    dma_offsets<D, false>(wave, lane, voff);
 
     // prologue: the first ST-1 tiles in flight
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
         if (i < n_tiles) {
-            dma_tile<D, true>(Kb, i * BN, Nk, kbuf[i], wave, lane);
-            dma_tile<D, false>(Vb, i * BN, Nk, vbuf[i], wave, lane);
+            dma_tile<D>(Kb, kv_bytes, koff, i * BN, kbuf[i], wave);
+            dma_tile<D>(Vb, kv_bytes, voff, i * BN, vbuf[i], wave);
         }
 
     // Iteration t: wait for tile t (own loads, then everyone's via the
@@ -354,8 +371,8 @@ __device__ __forceinline__ void attend_qtile(
             wait_vmcnt<0>();
         __syncthreads();
         if (t + ST - 1 < n_tiles) {
-            dma_tile<D, true>(Kb, (t + ST - 1) * BN, Nk, kfill, wave, lane);
-            dma_tile<D, false>(Vb, (t + ST - 1) * BN, Nk, vfill, wave, lane);
+            dma_tile<D>(Kb, kv_bytes, koff, (t + ST - 1) * BN, kfill, wave);
+            dma_tile<D>(Vb, kv_bytes, voff, (t + ST - 1) * BN, vfill, wave);
         }
         if (t < wave_tiles) {
             const int kt0 = t * BN;

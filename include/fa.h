@@ -86,7 +86,9 @@ extern "C" {
  *
  * A row with no valid key gets O = 0 and LSE = -inf.  B, H or Nq of 0 is an
  * empty problem (FA_OK, nothing written, pointers may be NULL).  Nk = 0 is
- * allowed (every row empty).  The library needs no workspace for this call.
+ * allowed (every row empty).  The keys of one (b, h) are addressed with
+ * 32-bit byte offsets: (Nk + 64) * d * 2 must stay below 2^31, else
+ * FA_ERR_SHAPE.  The library needs no workspace for this call.
  */
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
            int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype,

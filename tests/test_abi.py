@@ -75,6 +75,9 @@ def call_fwd(**over):
     (dict(lse=A + 2), fa.FA_ERR_ALIGN),
     (dict(kv_lens=A + 1), fa.FA_ERR_ALIGN),
     (dict(B=0x10000, H=0x10000, Nq=0x10000), fa.FA_ERR_SHAPE),
+    # the keys of one (b, h), plus one tile, are addressed with 32-bit byte offsets
+    (dict(Nk=(1 << 24) - 64, d=64), fa.FA_ERR_SHAPE),
+    (dict(Nk=(1 << 23) - 64, d=128), fa.FA_ERR_SHAPE),
     # empty problems: nothing to do, no pointer needed, no HIP call
     (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
     (dict(H=0, q=None, o=None, lse=None), fa.FA_OK),
