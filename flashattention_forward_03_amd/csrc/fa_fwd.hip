@@ -11,8 +11,9 @@
 // from-scratch page, kernel 1: causal tile-level skipping).
 //
 // gfx950 mapping:
-//   * workgroup = 4 waves = BM = 128 query rows (32 per wave), one (b, h);
-//     three workgroups per CU (one wave of each per SIMD);
+//   * workgroup = 4 waves = BM = 128 query rows (32 per wave) of one (b, h);
+//     three workgroups per CU (one wave of each per SIMD); causal tiles are
+//     dispatched heaviest first;
 //   * key tiles of BN = 64 rows.  K and V tiles are copied HBM/L2 -> LDS by
 //     the buffer-to-LDS load (16 bytes per lane, no VGPR staging); each lane
 //     fetches the chunk that belongs at its XOR-swizzled LDS slot, and rows
@@ -107,18 +108,42 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, unsigned (&off)[
     }
 }
 
+// The copy is issued with inline assembly on purpose: the compiler cannot
+// tell which LDS bytes a direct-to-LDS load writes, so for the builtin it
+// waits for the load (vmcnt(0)) before every later LDS read, which would
+// drain the prefetch ring on each tile.  Here every wait is explicit: a
+// tile is read only after wait_vmcnt for its own loads and a workgroup
+// barrier for the other waves' loads.
+typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource for the K (or V) rows of one (b, h): base, no stride,
+// nbytes in range (loads past it return zero), raw 32-bit dword format.
+__device__ __forceinline__ u32x4s_t make_rsrc(const void *base, int nbytes)
+{
+    const uint64_t a = (uint64_t)base;
+    u32x4s_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
 template <int D>
-__device__ __forceinline__ void dma_tile(const uint16_t *base, int nbytes, const unsigned *off,
-                                         int kt0, unsigned char *dst, int wave)
+__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, int kt0,
+                                         unsigned char *dst, int wave)
 {
     using G = Geometry<D>;
-#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists for the GPU target only
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, nbytes, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < G::PIECES_PER_WAVE; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(dst + (u * 4 + wave) * 1024), 16,
-                                                 off[u] + (unsigned)kt0 * G::ROWB, 0, 0, 0);
-#endif
+    for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
+        const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
+        const uint32_t voff = off[u] + (unsigned)kt0 * G::ROWB;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(lds_addr), "s"(rsrc)
+                     : "memory", "m0");
+    }
 }
 
 template <int D, bool BF16>
@@ -329,13 +354,6 @@ __device__ __forceinline__ void attend_qtile(
     const int wave_tiles = min(n_tiles, (wave_key_end + BN - 1) / BN);
 
     const int qrow = wave_first_row + l32;
-    u32x4_t qf[G::KSTEPS];
-    {
-        const uint16_t *qp = Q + (bh * Nq + (qrow < Nq ? qrow : 0)) * D + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < G::KSTEPS; ++c)
-            qf[c] = qrow < Nq ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
-    }
     int lim = kvlen;   // keys j < lim are valid for this lane's row
     if (causal)
         lim = min(lim, qrow + dq + 1);
@@ -347,7 +365,7 @@ __device__ __forceinline__ void attend_qtile(
     RowState st{-INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
-    const int kv_bytes = Nk * G::ROWB;
+    const u32x4s_t krs = make_rsrc(Kb, Nk * G::ROWB), vrs = make_rsrc(Vb, Nk * G::ROWB);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
     dma_offsets<D, true>(wave, lane, koff);
     dma_offsets<D, false>(wave, lane, voff);
@@ -356,9 +374,22 @@ __device__ __forceinline__ void attend_qtile(
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
         if (i < n_tiles) {
-            dma_tile<D>(Kb, kv_bytes, koff, i * BN, kbuf[i], wave);
-            dma_tile<D>(Vb, kv_bytes, voff, i * BN, vbuf[i], wave);
+            dma_tile<D>(krs, koff, i * BN, kbuf[i], wave);
+            dma_tile<D>(vrs, voff, i * BN, vbuf[i], wave);
         }
+
+    // Q after the prologue copies; the empty asm makes the compiler wait for
+    // it here, once, instead of at the loop head on every iteration
+    u32x4_t qf[G::KSTEPS];
+    {
+        const uint16_t *qp = Q + (bh * Nq + (qrow < Nq ? qrow : 0)) * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            qf[c] = qrow < Nq ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            asm volatile("" : "+v"(qf[c]));
+    }
 
     // Iteration t: wait for tile t (own loads, then everyone's via the
     // barrier), refill the ring slot freed by tile t-1 with tile t+ST-1,
@@ -371,8 +402,8 @@ __device__ __forceinline__ void attend_qtile(
             wait_vmcnt<0>();
         __syncthreads();
         if (t + ST - 1 < n_tiles) {
-            dma_tile<D>(Kb, kv_bytes, koff, (t + ST - 1) * BN, kfill, wave);
-            dma_tile<D>(Vb, kv_bytes, voff, (t + ST - 1) * BN, vfill, wave);
+            dma_tile<D>(krs, koff, (t + ST - 1) * BN, kfill, wave);
+            dma_tile<D>(vrs, voff, (t + ST - 1) * BN, vfill, wave);
         }
         if (t < wave_tiles) {
             const int kt0 = t * BN;
@@ -431,11 +462,13 @@ __device__ __forceinline__ void attend_qtile(
     }
 }
 
-// Work decomposition: one workgroup per (b, h, unit).  Causal: a unit is the
-// pair of query tiles j and n_qtiles-1-j (the middle tile alone when
-// n_qtiles is odd), so every workgroup visits the same number of key tiles.
-// Non-causal: a unit is one query tile.  Work ids are renumbered so that
-// each XCD receives a contiguous range (units of one head share its L2).
+// Work decomposition: one workgroup per (b, h, query tile).  Causal: tile
+// qt = n_qtiles-1 - blockIdx / (B*H), so the heaviest tiles (most key tiles)
+// are dispatched first and the dispatcher fills the GPU longest job first;
+// the light diagonal-corner tiles form the tail.  blockIdx % (B*H) picks the
+// head, and since workgroups go to XCD blockIdx % 8, all tiles of one head
+// share an XCD (and its L2) whenever B*H is a multiple of 8.  Non-causal:
+// work ids are renumbered so that each XCD receives a contiguous range.
 // The causal flag is a runtime argument: both modes share one code path.
 template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
@@ -461,9 +494,19 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool causal = causal_flag != 0;
 
-    const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
-    const int bhi = logical / n_units;
-    const int unit = logical - bhi * n_units;
+    int bhi, qt;
+    if (causal) {
+        // one query tile per workgroup, heaviest tiles first, so the dispatcher
+        // fills the GPU longest job first; blockIdx % (B*H) picks the head, so
+        // with B*H a multiple of 8 all tiles of a head share one XCD
+        const int BHn = gridDim.x / n_qtiles;
+        bhi = blockIdx.x % BHn;
+        qt = n_qtiles - 1 - blockIdx.x / BHn;
+    } else {
+        const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
+        bhi = logical / n_units;
+        qt = logical - bhi * n_units;
+    }
     const size_t bh = (size_t)bhi;
     const int b = bhi / H;
     int kvlen = Nk;
@@ -474,19 +517,15 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const uint16_t *Kb = K + bh * Nk * D;
     const uint16_t *Vb = V + bh * Nk * D;
 
-    // causal: tile n_qtiles-1-unit (the longer one) first, then tile unit
-    const int n_pass = (causal && unit != n_qtiles - 1 - unit) ? 2 : 1;
-    for (int pass = 0; pass < n_pass; ++pass) {
-        const int qt = causal ? (pass == 0 ? n_qtiles - 1 - unit : unit) : unit;
-        attend_qtile<D, BF16>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal, kbuf,
-                              vbuf, wave, lane);
-    }
+    attend_qtile<D, BF16>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal, kbuf, vbuf,
+                          wave, lane);
 }
 
 int units_per_head(int Nq, bool causal)
 {
     const int n_qtiles = (Nq + BM - 1) / BM;
-    return causal ? (n_qtiles + 1) / 2 : n_qtiles;
+    (void)causal;
+    return n_qtiles;
 }
 
 template <int D, bool BF16>
