@@ -152,6 +152,33 @@ def test_large_scores_stay_finite_and_shift_lse():
     compare(o2, l2, o_ref, l_ref, "shifted keys")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_running_max_moves_mid_row(dtype):
+    """Keys step up in every coordinate at each 64-key tile, so with positive
+    queries a row's maximum score grows by ~6.5 (bf16) / ~3.2 (f16) log2 units
+    per tile: the probabilities formed against a stale maximum pass the 2^32 /
+    2^15 bound every few tiles and the exact update (new maximum, rescale of O
+    and l) runs in the middle of every row, many times.  O and LSE must still
+    match the oracle."""
+    B, H, N, d = 1, 2, 640, 64
+    rng = np.random.default_rng(905)
+    qf = (np.round(rng.uniform(0.25, 2, (B, H, N, d)) * 4) / 4).astype(np.float32)
+    step = 0.5 if dtype == "bf16" else 0.25          # grid on which k stays exact
+    kf = (np.round(rng.uniform(-2, 2, (B, H, N, d)) / step) * step).astype(np.float32)
+    kf += (step * (np.arange(N) // 64)).astype(np.float32)[None, None, :, None]
+    for causal, lens in ((True, None), (False, (N - 100, N))):
+        w = gen.fwd_inputs(B, H, N, N, d, dtype, 905, causal=causal, scale=0.125, kv_len_range=lens)
+        w.q[...] = gen.float_to_bits_exact(qf, dtype)
+        w.k[...] = gen.float_to_bits_exact(kf, dtype)
+        # V halved (exact): with a few dominant keys per row, the 16-bit rounding
+        # of P alone puts ~|v|*2^-9 into O; the test is about the maximum
+        w.v[...] = gen.float_to_bits_exact(gen.bits_to_float(w.v, dtype) * 0.5, dtype)
+        o, lse = gpu_forward(w)
+        o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, dtype, 0.125, causal, w.kv_lens)
+        print(dtype, "causal" if causal else "padded", compare(o, lse, o_ref, lse_ref, "moving max"),
+              flush=True)
+
+
 def test_bitwise_deterministic():
     import torch
 
