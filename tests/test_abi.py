@@ -101,9 +101,9 @@ def call_dec(**over):
 
 
 def test_decode_workspace_size(lib):
-    # 100 pages -> 4 chunks of 32 pages; per (s,h,chunk): d floats + (max, sum)
-    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 16) == 2 * 2 * 4 * (128 + 2) * 4
-    assert fa.fa_decode_workspace_bytes(2, 2, 128, 32, 16) == 0      # one chunk: none needed
+    # 100 pages -> 7 chunks of 16 pages; per (s,h,chunk): d floats + (max, sum)
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 16) == 2 * 2 * 7 * (128 + 2) * 4
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 16, 16) == 0      # one chunk: none needed
     assert fa.fa_decode_workspace_bytes(2, 2, 96, 100, 16) == 0      # unsupported -> 0
     assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 8) == 0
 

@@ -172,7 +172,7 @@ def test_running_max_moves_mid_row(dtype):
         w.k[...] = gen.float_to_bits_exact(kf, dtype)
         # V halved (exact): with a few dominant keys per row, the 16-bit rounding
         # of P alone puts ~|v|*2^-9 into O; the test is about the maximum
-        w.v[...] = gen.float_to_bits_exact(gen.bits_to_float(w.v, dtype) * 0.5, dtype)
+        w.v[...] = gen.round_bits(gen.bits_to_float(w.v, dtype) * 0.5, dtype)
         o, lse = gpu_forward(w)
         o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, dtype, 0.125, causal, w.kv_lens)
         print(dtype, "causal" if causal else "padded", compare(o, lse, o_ref, lse_ref, "moving max"),
