@@ -228,42 +228,98 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
     }
 }
 
-// Merge the chunk partials of each (sequence, head); write empty sequences.
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const int32_t *__restrict__ kv_lens,
-                                                           const float *__restrict__ part_o,
-                                                           const float *__restrict__ part_ml,
-                                                           float *__restrict__ O, float *__restrict__ LSE,
-                                                           int H, int max_pages, int max_chunks)
+// Wave-wide max / sum (all 64 lanes hold the result).
+__device__ __forceinline__ float wave_max(float x)
 {
-    const int sh = blockIdx.x;
-    const int s = sh / H;
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));   // xor 16
+    return fmaxf(x, other_half(x));
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    return x + other_half(x);
+}
+
+// Merge the chunk partials of each (sequence, head) with the log-sum-exp
+// rule; write empty sequences.  One workgroup per (sequence, group of 4
+// heads), one wave per head: the lanes load all chunks' (m, l) at once, and
+// the chunk weights are broadcast with readlane for the weighted sum of the
+// partial outputs (lanes over head dims).
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const int32_t *__restrict__ kv_lens,
+                                                                  const float *__restrict__ part_o,
+                                                                  const float *__restrict__ part_ml,
+                                                                  float *__restrict__ O, float *__restrict__ LSE,
+                                                                  int H, int n_hgroups, int max_pages, int max_chunks)
+{
+    constexpr int DPL = D / 64;
+    const int s = blockIdx.x / n_hgroups, hg = blockIdx.x - s * n_hgroups;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int h = hg * GROUP + wave;
+    if (h >= H)
+        return;
+    const size_t sh = (size_t)s * H + h;
     int kvlen = kv_lens[s];
     kvlen = kvlen < 0 ? 0 : (kvlen > max_pages * PAGE ? max_pages * PAGE : kvlen);
     const int npages = (kvlen + PAGE - 1) / PAGE;
     const int nchunks = (npages + kDecodeChunkPages - 1) / kDecodeChunkPages;
-    const int tid = threadIdx.x;
     if (nchunks == 1)
-        return;
+        return;   // finished by the split kernel
     if (nchunks == 0) {
-        O[(size_t)sh * D + tid] = 0.f;
-        if (tid == 0)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+            O[sh * D + lane + 64 * k] = 0.f;
+        if (lane == 0)
             LSE[sh] = -INFINITY;
         return;
     }
-    const float *ml = part_ml + (size_t)sh * max_chunks * 2;
-    const float *po = part_o + (size_t)sh * max_chunks * D;
+    const float *ml = part_ml + sh * max_chunks * 2;
+    const float *po = part_o + sh * max_chunks * D;
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+        acc[k] = 0.f;
+    // chunks in groups of 64 (one per lane); M over all chunks first
     float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c)
-        M = fmaxf(M, ml[2 * c]);
-    float L = 0.f, num = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-        const float w = fast_exp2(ml[2 * c] - M);
-        L = fmaf(w, ml[2 * c + 1], L);
-        num = fmaf(w, po[(size_t)c * D + tid], num);
+    for (int c0 = 0; c0 < nchunks; c0 += 64)
+        M = fmaxf(M, wave_max(c0 + lane < nchunks ? ml[2 * (c0 + lane)] : -INFINITY));
+    float L = 0.f;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+        const int c = c0 + lane;
+        const float w = c < nchunks ? fast_exp2(ml[2 * c] - M) : 0.f;
+        L += wave_sum(c < nchunks ? w * ml[2 * c + 1] : 0.f);
+        const int n = min(64, nchunks - c0);
+        // 16 chunks' partial rows are loaded before any is used
+        for (int j0 = 0; j0 < n; j0 += 16) {
+            float v[16][DPL];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int k = 0; k < DPL; ++k)
+                    v[j][k] = j0 + j < n ? po[(size_t)(c0 + j0 + j) * D + lane + 64 * k] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + j));
+#pragma unroll
+                for (int k = 0; k < DPL; ++k)
+                    acc[k] = fmaf(wj, v[j][k], acc[k]);
+            }
+        }
     }
-    O[(size_t)sh * D + tid] = num / L;
-    if (tid == 0)
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+        O[sh * D + lane + 64 * k] = acc[k] * inv;
+    if (lane == 0)
         LSE[sh] = (M + __log2f(L)) * kLn2;
 }
 
@@ -280,8 +336,8 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.S * a.H)), dim3(D), 0, stream,
-                       a.kv_lens, a.part_o, a.part_ml, a.o, a.lse, a.H, a.max_pages, max_chunks);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.S * n_hgroups)), dim3(NTHREADS), 0, stream,
+                       a.kv_lens, a.part_o, a.part_ml, a.o, a.lse, a.H, n_hgroups, a.max_pages, max_chunks);
     return hipGetLastError();
 }
 
