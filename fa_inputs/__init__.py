@@ -12,12 +12,13 @@ Recipe (every workload):
     f16 through numpy's ``astype(float16)``, bf16 through torch's CPU
     ``to(bfloat16)``.  Tensors carry raw 16-bit patterns (``uint16``) so
     that both sides decode the very same bits.
-  * Forward draw order: Q, K, V (each full ``[B, H, N, d]`` row-major),
-    then the key lengths ``integers(lo, hi, endpoint=True)`` when a padding
-    range is given.
+  * Forward draw order: Q ``[B, H, Nq, d]``, K, V (each ``[B, Hkv, Nk, d]``
+    row-major; Hkv = H unless grouped-query heads are asked for), then the
+    key lengths ``integers(lo, hi, endpoint=True)`` when a padding range is
+    given.
   * Decode draw order: lengths ``kv_len[S]`` (inclusive range), q ``[S, H, d]``,
     K then V for all cached tokens concatenated over sequences
-    (``[sum(kv_len), H, d]``), then the page placement: a seeded permutation
+    (``[sum(kv_len), Hkv, d]``), then the page placement: a seeded permutation
     of the page pool; sequence s's p-th logical page goes to
     ``perm[sum_{s'<s} ceil(kv_len[s']/page) + p]``.
 
@@ -86,8 +87,8 @@ def to_torch(bits: np.ndarray, dtype: str):
 @dataclasses.dataclass
 class FwdInputs:
     q: np.ndarray            # uint16 [B, H, Nq, d]
-    k: np.ndarray            # uint16 [B, H, Nk, d]
-    v: np.ndarray            # uint16 [B, H, Nk, d]
+    k: np.ndarray            # uint16 [B, Hkv, Nk, d]
+    v: np.ndarray            # uint16 [B, Hkv, Nk, d]
     dtype: str
     scale: float
     causal: bool
@@ -99,14 +100,21 @@ class FwdInputs:
         B, H, Nq, d = self.q.shape
         return B, H, Nq, self.k.shape[2], d
 
+    @property
+    def Hkv(self):
+        return self.k.shape[1]
+
 
 def fwd_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int, *,
                causal: bool, scale: Optional[float] = None,
-               kv_len_range: Optional[tuple] = None) -> FwdInputs:
+               kv_len_range: Optional[tuple] = None, Hkv: Optional[int] = None) -> FwdInputs:
+    Hkv = H if Hkv is None else Hkv
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
     rng = np.random.default_rng(seed)
     q = round_bits(rng.standard_normal((B, H, Nq, d), dtype=np.float32), dtype)
-    k = round_bits(rng.standard_normal((B, H, Nk, d), dtype=np.float32), dtype)
-    v = round_bits(rng.standard_normal((B, H, Nk, d), dtype=np.float32), dtype)
+    k = round_bits(rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32), dtype)
+    v = round_bits(rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32), dtype)
     kv_lens = None
     if kv_len_range is not None:
         lo, hi = kv_len_range
@@ -121,8 +129,8 @@ def fwd_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int, 
 @dataclasses.dataclass
 class DecodeInputs:
     q: np.ndarray            # uint16 [S, H, d]
-    k: np.ndarray            # uint16 [T, H, d], sequences concatenated
-    v: np.ndarray            # uint16 [T, H, d]
+    k: np.ndarray            # uint16 [T, Hkv, d], sequences concatenated
+    v: np.ndarray            # uint16 [T, Hkv, d]
     seq_off: np.ndarray      # int64 [S+1]; sequence s owns tokens seq_off[s]:seq_off[s+1]
     kv_lens: np.ndarray      # int32 [S]
     page_table: np.ndarray   # int32 [S, max_pages]; -1 where unused
@@ -141,6 +149,10 @@ class DecodeInputs:
         return self.q.shape[1]
 
     @property
+    def Hkv(self):
+        return self.k.shape[1]
+
+    @property
     def d(self):
         return self.q.shape[2]
 
@@ -152,16 +164,20 @@ def pages_per_seq(kv_lens: np.ndarray, page_size: int) -> np.ndarray:
 def decode_inputs(S: int, H: int, d: int, len_range: tuple, dtype: str, seed: int, *,
                   page_size: int = 16, num_pages: int = 1 << 16,
                   max_pages: Optional[int] = None, scale: Optional[float] = None,
-                  identity_pages: bool = False) -> DecodeInputs:
+                  identity_pages: bool = False, Hkv: Optional[int] = None) -> DecodeInputs:
     """Draw one decode batch.  ``identity_pages`` keeps the same draws but lays
-    the sequences' pages out contiguously (page p of the pool in logical order)."""
+    the sequences' pages out contiguously (page p of the pool in logical order).
+    ``Hkv``: number of K/V heads (default H)."""
+    Hkv = H if Hkv is None else Hkv
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
     rng = np.random.default_rng(seed)
     lo, hi = len_range
     kv_lens = rng.integers(lo, hi, size=S, endpoint=True).astype(np.int32)
     q = round_bits(rng.standard_normal((S, H, d), dtype=np.float32), dtype)
     T = int(kv_lens.sum())
-    k = round_bits(rng.standard_normal((T, H, d), dtype=np.float32), dtype)
-    v = round_bits(rng.standard_normal((T, H, d), dtype=np.float32), dtype)
+    k = round_bits(rng.standard_normal((T, Hkv, d), dtype=np.float32), dtype)
+    v = round_bits(rng.standard_normal((T, Hkv, d), dtype=np.float32), dtype)
     perm = rng.permutation(num_pages).astype(np.int64)
     if identity_pages:
         perm = np.arange(num_pages, dtype=np.int64)
@@ -199,14 +215,14 @@ def page_slots(inp: DecodeInputs):
 
 
 def build_pool_host(inp: DecodeInputs, which: str, fill_bits: int = 0) -> np.ndarray:
-    """Scatter the logical K (or V) into a host pool ``[num_pages, H, page, d]``.
+    """Scatter the logical K (or V) into a host pool ``[num_pages, Hkv, page, d]``.
 
     Slots not holding a cached token keep ``fill_bits`` (0 = +0.0; a NaN
     pattern for the poison test).  Only for small pools: the full-size pool
     is built on the device by :func:`build_pool_device`.
     """
     src = inp.k if which == "k" else inp.v
-    pool = np.full((inp.num_pages, inp.H, inp.page_size, inp.d), fill_bits, dtype=np.uint16)
+    pool = np.full((inp.num_pages, inp.Hkv, inp.page_size, inp.d), fill_bits, dtype=np.uint16)
     phys, row = page_slots(inp)
     pool[phys, :, row, :] = src
     return pool
@@ -217,7 +233,7 @@ def build_pool_device(inp: DecodeInputs, which: str, device, fill_bits: int = 0)
     import torch
 
     tdt = torch.float16 if inp.dtype == "f16" else torch.bfloat16
-    pool = torch.empty((inp.num_pages, inp.H, inp.page_size, inp.d), dtype=torch.int16,
+    pool = torch.empty((inp.num_pages, inp.Hkv, inp.page_size, inp.d), dtype=torch.int16,
                        device=device)
     pool.fill_(int(np.array(fill_bits, np.uint16).view(np.int16)))
     phys, row = page_slots(inp)

@@ -31,9 +31,9 @@ def _load():
         I = ctypes.c_int
         L = ctypes.c_int64
         D = ctypes.c_double
-        lib.oracle_fwd.argtypes = [P, P, P, I, I, I, I, I, I, D, I, P, P, L, P, P, I]
+        lib.oracle_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, D, I, P, P, L, P, P, I]
         lib.oracle_fwd.restype = I
-        lib.oracle_decode.argtypes = [P, P, P, P, I, I, I, I, D, P, P, I]
+        lib.oracle_decode.argtypes = [P, P, P, P, I, I, I, I, I, D, P, P, I]
         lib.oracle_decode.restype = I
         lib.oracle_widen.argtypes = [P, I, L, P]
         lib.oracle_widen.restype = None
@@ -58,7 +58,8 @@ def attention_fwd(q, k, v, dtype: str, scale: float, causal: bool,
                   rows: Optional[np.ndarray] = None, nthreads: int = 0):
     """O (float64) and LSE (float64) of exact attention.
 
-    q: [B,H,Nq,d], k/v: [B,H,Nk,d] uint16 bits.  ``rows``: optional flat row
+    q: [B,H,Nq,d], k/v: [B,Hkv,Nk,d] uint16 bits, H a multiple of Hkv; query
+    head h reads K/V head h // (H // Hkv).  ``rows``: optional flat row
     ids (b*H+h)*Nq+i; then O is [len(rows), d] and LSE [len(rows)] in the
     given order, else O is [B,H,Nq,d] and LSE [B,H,Nq].
     """
@@ -66,16 +67,17 @@ def attention_fwd(q, k, v, dtype: str, scale: float, causal: bool,
     k = np.ascontiguousarray(k, np.uint16)
     v = np.ascontiguousarray(v, np.uint16)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    assert k.shape == (B, H, Nk, d) and v.shape == k.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    assert Hkv >= 1 and H % Hkv == 0
+    assert k.shape == (B, Hkv, Nk, d) and v.shape == k.shape
     kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, np.int32)
     if kl is not None:
         assert kl.shape == (B,)
     if rows is None:
         o = np.empty((B, H, Nq, d), np.float64)
         lse = np.empty((B, H, Nq), np.float64)
-        rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, H, Nq, Nk, d,
-                                float(scale), int(bool(causal)), _ptr(kl), None, 0,
+        rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, H, Hkv, Nq, Nk,
+                                d, float(scale), int(bool(causal)), _ptr(kl), None, 0,
                                 _ptr(o), _ptr(lse), nthreads)
     else:
         rows = np.asarray(rows, np.int64).reshape(-1)
@@ -84,8 +86,8 @@ def attention_fwd(q, k, v, dtype: str, scale: float, causal: bool,
         assert srt.size == 0 or (srt[0] >= 0 and srt[-1] < B * H * Nq)
         o_s = np.empty((srt.size, d), np.float64)
         lse_s = np.empty((srt.size,), np.float64)
-        rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, H, Nq, Nk, d,
-                                float(scale), int(bool(causal)), _ptr(kl), _ptr(srt),
+        rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, H, Hkv, Nq, Nk,
+                                d, float(scale), int(bool(causal)), _ptr(kl), _ptr(srt),
                                 srt.size, _ptr(o_s), _ptr(lse_s), nthreads)
         o = np.empty_like(o_s)
         lse = np.empty_like(lse_s)
@@ -99,7 +101,8 @@ def attention_fwd(q, k, v, dtype: str, scale: float, causal: bool,
 def decode(q, k, v, seq_off, dtype: str, scale: float, nthreads: int = 0):
     """Decode attention over logical per-sequence caches.
 
-    q: [S,H,d]; k/v: [T,H,d] with sequence s owning rows seq_off[s]:seq_off[s+1].
+    q: [S,H,d]; k/v: [T,Hkv,d] with sequence s owning rows seq_off[s]:seq_off[s+1],
+    H a multiple of Hkv; query head h reads K/V head h // (H // Hkv).
     Returns O [S,H,d] and LSE [S,H] (float64).
     """
     q = np.ascontiguousarray(q, np.uint16)
@@ -107,11 +110,13 @@ def decode(q, k, v, seq_off, dtype: str, scale: float, nthreads: int = 0):
     v = np.ascontiguousarray(v, np.uint16)
     off = np.ascontiguousarray(seq_off, np.int64)
     S, H, d = q.shape
-    assert off.shape == (S + 1,) and k.shape == (int(off[-1]), H, d) and v.shape == k.shape
+    Hkv = k.shape[1]
+    assert Hkv >= 1 and H % Hkv == 0
+    assert off.shape == (S + 1,) and k.shape == (int(off[-1]), Hkv, d) and v.shape == k.shape
     o = np.empty((S, H, d), np.float64)
     lse = np.empty((S, H), np.float64)
-    rc = _load().oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(off), _DT[dtype], S, H, d,
-                               float(scale), _ptr(o), _ptr(lse), nthreads)
+    rc = _load().oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(off), _DT[dtype], S, H, Hkv,
+                               d, float(scale), _ptr(o), _ptr(lse), nthreads)
     if rc != 0:
         raise RuntimeError(f"oracle_decode self-check failed ({rc})")
     return o, lse

@@ -26,6 +26,11 @@
  * computation with every cached token valid; it reads the LOGICAL per
  * sequence K/V, never a paged pool.
  *
+ * Grouped-query attention (the MQA / GQA variants of the llm-kernel-lib
+ * page's "Ablation Study"): K and V have Hkv heads, H a multiple of Hkv, and
+ * query head h attends with key/value head h / (H / Hkv) -- consecutive
+ * query heads share one K/V head.  Hkv = H is ordinary multi-head attention.
+ *
  * Inputs are raw f16 / bf16 bit patterns; they are widened exactly to
  * double here.  All arithmetic is IEEE double, libm exp/log, no fast-math.
  */
@@ -123,7 +128,7 @@ static int attention_row(const double *q, const double *kk, const double *vv, in
 
 typedef struct {
     const uint16_t *q, *k, *v;
-    int dtype, B, H, Nq, Nk, d, causal;
+    int dtype, B, H, Hkv, Nq, Nk, d, causal;
     double scale;
     const int32_t *kv_lens;
     const int64_t *rows;   /* sorted flat row ids (b*H+h)*Nq+i, or NULL = all */
@@ -159,7 +164,8 @@ static void *fwd_worker(void *arg)
         goto done;
     }
     for (int64_t bh = J->tid; bh < (int64_t)J->B * J->H; bh += J->nthreads) {
-        int b = (int)(bh / J->H);
+        int b = (int)(bh / J->H), h = (int)(bh % J->H);
+        int64_t kvh = (int64_t)b * J->Hkv + h / (J->H / J->Hkv);   /* K/V head of query head h */
         int64_t r0, r1;   /* positions in the output for this (b,h) */
         if (J->rows) {
             r0 = lower_bound64(J->rows, J->nrows, bh * Nq);
@@ -170,8 +176,8 @@ static void *fwd_worker(void *arg)
         }
         if (r0 == r1)
             continue;
-        oracle_widen(J->k + bh * Nk * d, J->dtype, (int64_t)Nk * d, kk);
-        oracle_widen(J->v + bh * Nk * d, J->dtype, (int64_t)Nk * d, vv);
+        oracle_widen(J->k + kvh * Nk * d, J->dtype, (int64_t)Nk * d, kk);
+        oracle_widen(J->v + kvh * Nk * d, J->dtype, (int64_t)Nk * d, vv);
         int nb = J->kv_lens ? J->kv_lens[b] : Nk;
         if (nb > Nk)
             nb = Nk;
@@ -208,17 +214,20 @@ static int thread_count(int requested)
 }
 
 /*
- * Exact attention forward.  q [B,H,Nq,d], k/v [B,H,Nk,d] (f16/bf16 bits).
+ * Exact attention forward.  q [B,H,Nq,d], k/v [B,Hkv,Nk,d] (f16/bf16 bits),
+ * H a multiple of Hkv.
  * rows: NULL for every row, else nrows sorted flat ids (b*H+h)*Nq+i; the
  * outputs o [nrows or B*H*Nq, d] and lse [nrows or B*H*Nq] follow that order.
  * Returns the number of rows failing the softmax self-check (0 expected),
  * or -1 on allocation failure.
  */
 int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype, int B,
-               int H, int Nq, int Nk, int d, double scale, int causal,
+               int H, int Hkv, int Nq, int Nk, int d, double scale, int causal,
                const int32_t *kv_lens, const int64_t *rows, int64_t nrows, double *o,
                double *lse, int nthreads)
 {
+    if (Hkv < 1 || H % Hkv != 0)
+        return -2;
     int nt = thread_count(nthreads);
     if ((int64_t)nt > (int64_t)B * H)
         nt = B * H > 0 ? B * H : 1;
@@ -230,7 +239,7 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtyp
         return -1;
     }
     for (int t = 0; t < nt; ++t) {
-        fwd_job J = {q, k, v, dtype, B, H, Nq, Nk, d, causal, scale, kv_lens,
+        fwd_job J = {q, k, v, dtype, B, H, Hkv, Nq, Nk, d, causal, scale, kv_lens,
                      rows, nrows, o, lse, nt, t, 0};
         jobs[t] = J;
         pthread_create(&th[t], NULL, fwd_worker, &jobs[t]);
@@ -253,7 +262,7 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtyp
 typedef struct {
     const uint16_t *q, *k, *v;
     const int64_t *seq_off;
-    int dtype, S, H, d;
+    int dtype, S, H, Hkv, d;
     double scale;
     double *o, *lse;
     int nthreads, tid, bad;
@@ -278,12 +287,13 @@ static void *dec_worker(void *arg)
     }
     for (int64_t sh = J->tid; sh < (int64_t)J->S * H; sh += J->nthreads) {
         int sq = (int)(sh / H), h = (int)(sh % H);
+        int kvh = h / (H / J->Hkv);   /* K/V head of query head h */
         int64_t a = J->seq_off[sq];
         int n = (int)(J->seq_off[sq + 1] - a);
-        /* token t of sequence sq, head h: row (a+t)*H + h of the [T,H,d] arrays */
+        /* token t of sequence sq, K/V head kvh: row (a+t)*Hkv + kvh of the [T,Hkv,d] arrays */
         for (int t = 0; t < n; ++t) {
-            oracle_widen(J->k + ((a + t) * H + h) * d, J->dtype, d, kk + (int64_t)t * d);
-            oracle_widen(J->v + ((a + t) * H + h) * d, J->dtype, d, vv + (int64_t)t * d);
+            oracle_widen(J->k + ((a + t) * J->Hkv + kvh) * d, J->dtype, d, kk + (int64_t)t * d);
+            oracle_widen(J->v + ((a + t) * J->Hkv + kvh) * d, J->dtype, d, vv + (int64_t)t * d);
         }
         oracle_widen(J->q + sh * d, J->dtype, d, qq);
         J->bad += attention_row(qq, kk, vv, n, d, J->scale, s, J->o + sh * d, J->lse + sh);
@@ -297,13 +307,15 @@ done:
 }
 
 /*
- * Decode attention: q [S,H,d]; k/v [T,H,d] with sequence s owning tokens
+ * Decode attention: q [S,H,d]; k/v [T,Hkv,d] with sequence s owning tokens
  * seq_off[s] .. seq_off[s+1]-1 (all of them attended).  o [S,H,d], lse [S,H].
  */
 int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  const int64_t *seq_off, int dtype, int S, int H, int d, double scale,
+                  const int64_t *seq_off, int dtype, int S, int H, int Hkv, int d, double scale,
                   double *o, double *lse, int nthreads)
 {
+    if (Hkv < 1 || H % Hkv != 0)
+        return -2;
     int nt = thread_count(nthreads);
     if ((int64_t)nt > (int64_t)S * H)
         nt = S * H > 0 ? S * H : 1;
@@ -315,7 +327,7 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         return -1;
     }
     for (int t = 0; t < nt; ++t) {
-        dec_job J = {q, k, v, seq_off, dtype, S, H, d, scale, o, lse, nt, t, 0};
+        dec_job J = {q, k, v, seq_off, dtype, S, H, Hkv, d, scale, o, lse, nt, t, 0};
         jobs[t] = J;
         pthread_create(&th[t], NULL, dec_worker, &jobs[t]);
     }

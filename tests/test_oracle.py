@@ -353,3 +353,89 @@ def test_decode_equals_forward_with_one_query():
                                       True)
         np.testing.assert_allclose(fo[0, :, 0], o[s], atol=1e-15, rtol=0)
         np.testing.assert_allclose(fl[0, :, 0], lse[s], atol=1e-15, rtol=0)
+
+
+# ------------------------------------------------- grouped-query heads ---
+# MQA / GQA (llm-kernel-lib page, "Ablation Study"): K/V carry Hkv heads and
+# query head h reads K/V head h // (H // Hkv).
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 3), (4, 1), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_matches_brute_force_with_head_map(H, Hkv, causal):
+    rng = np.random.default_rng(40 + H + 10 * Hkv + causal)
+    B, Nq, Nk, d = 2, 5, 7, 4
+    q = _draw(rng, (B, H, Nq, d), "bf16")
+    k = _draw(rng, (B, Hkv, Nk, d), "bf16")
+    v = _draw(rng, (B, Hkv, Nk, d), "bf16")
+    kv_lens = np.array([7, 4], np.int32)
+    o, lse = oracle.attention_fwd(q, k, v, "bf16", 0.5, causal, kv_lens)
+    qf, kf, vf = _f(q, "bf16"), _f(k, "bf16"), _f(v, "bf16")
+    g = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            bo, bl = brute.attention(qf[b, h].tolist(), kf[b, h // g].tolist(),
+                                     vf[b, h // g].tolist(), 0.5, causal, int(kv_lens[b]))
+            assert np.max(np.abs(np.array(bl) - lse[b, h])) <= 1e-12
+            assert np.max(np.abs(np.array(bo) - o[b, h])) <= 1e-12
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 4])
+def test_gqa_forward_equals_mha_on_repeated_heads(Hkv):
+    inp = gen.fwd_inputs(2, 8, 33, 40, 16, "f16", 50 + Hkv, causal=True, Hkv=Hkv,
+                         kv_len_range=(20, 40))
+    g = 8 // Hkv
+    a = oracle.attention_fwd(inp.q, inp.k, inp.v, "f16", inp.scale, True, inp.kv_lens)
+    b = oracle.attention_fwd(inp.q, np.repeat(inp.k, g, axis=1), np.repeat(inp.v, g, axis=1),
+                             "f16", inp.scale, True, inp.kv_lens)
+    # the same per-head arithmetic on the same K/V rows: identical bits
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_mqa_equal_query_heads_give_equal_outputs():
+    rng = np.random.default_rng(60)
+    q1 = _draw(rng, (1, 1, 9, 8), "bf16")
+    q = np.repeat(q1, 4, axis=1)
+    k = _draw(rng, (1, 1, 11, 8), "bf16")
+    v = _draw(rng, (1, 1, 11, 8), "bf16")
+    o, lse = oracle.attention_fwd(q, k, v, "bf16", 0.4, False)
+    for h in range(1, 4):
+        assert np.array_equal(o[0, h], o[0, 0]) and np.array_equal(lse[0, h], lse[0, 0])
+
+
+def test_gqa_decode_matches_brute_force_with_head_map():
+    inp = gen.decode_inputs(3, 6, 8, (1, 37), "bf16", 61, page_size=4, num_pages=64, Hkv=2)
+    o, lse = oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, "bf16", inp.scale)
+    qf, kf, vf = _f(inp.q, "bf16"), _f(inp.k, "bf16"), _f(inp.v, "bf16")
+    for s in range(inp.S):
+        a, b = inp.seq_off[s], inp.seq_off[s + 1]
+        for h in range(inp.H):
+            bo, bl = brute.attention([qf[s, h].tolist()], kf[a:b, h // 3].tolist(),
+                                     vf[a:b, h // 3].tolist(), inp.scale)
+            assert abs(bl[0] - lse[s, h]) <= 1e-12
+            assert np.max(np.abs(np.array(bo[0]) - o[s, h])) <= 1e-12
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 4])
+def test_gqa_decode_equals_mha_on_repeated_heads(Hkv):
+    inp = gen.decode_inputs(4, 8, 16, (1, 70), "f16", 62 + Hkv, page_size=8, num_pages=64,
+                            Hkv=Hkv)
+    g = 8 // Hkv
+    a = oracle.decode(inp.q, inp.k, inp.v, inp.seq_off, "f16", inp.scale)
+    b = oracle.decode(inp.q, np.repeat(inp.k, g, axis=1), np.repeat(inp.v, g, axis=1),
+                      inp.seq_off, "f16", inp.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_gqa_pool_round_trip():
+    inp = gen.decode_inputs(3, 8, 8, (1, 37), "bf16", 63, page_size=4, num_pages=64, Hkv=2)
+    for which, src in (("k", inp.k), ("v", inp.v)):
+        pool = gen.build_pool_host(inp, which)
+        assert pool.shape == (64, 2, 4, 8)
+        assert np.array_equal(gen.gather_logical(pool, inp), src)
+
+
+def test_gqa_rejects_head_counts_that_do_not_divide():
+    with pytest.raises(ValueError):
+        gen.fwd_inputs(1, 6, 4, 4, 8, "bf16", 0, causal=False, Hkv=4)
+    with pytest.raises(ValueError):
+        gen.decode_inputs(1, 6, 8, (1, 4), "bf16", 0, Hkv=4)
