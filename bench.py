@@ -7,13 +7,16 @@ already resident in HBM:
     the headline TFLOP/s is quoted on), and
   * fa_decode_paged on the decode batch (32 sequences x 32 heads, d=128,
     lengths uniform in [512, 8192], 16-token pages scattered over a
-    65536-page pool).
+    65536-page pool), and
+  * fa_decode_paged_gqa on the same kind of batch with 32 query heads over
+    8 K/V heads (grouped-query attention).
 Each kernel is bracketed by HIP events on the stream it is launched on.
 
 Prints ONE JSON line.  ``value`` is forward TFLOP/s (nominal FLOPs
 4*B*H*Nq*Nk*d, halved for causal, over the forward's average event time);
 ``roofline`` is the forward kernel against the dense bf16 MFMA peak;
-``decode`` carries the decode GB/s against the 8 TB/s HBM peak; and
+``decode`` and ``decode_gqa`` carry the decode GB/s against the 8 TB/s HBM
+peak; and
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 forward workload on the host cores (and reports the sample's parity).
 """
@@ -37,12 +40,14 @@ import fa_inputs as gen  # noqa: E402
 
 FWD_WORKLOAD = "fwd_causal_b8h16_n4096_d64_bf16"
 DEC_WORKLOAD = "decode_paged_s32h32_d128_bf16"
+GQA_WORKLOAD = "decode_paged_s32h32kv8_d128_bf16"
 
 # MI355X published peaks (dense, no sparsity)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_causal_b8h16_n4096_d64.json")
 DEC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_paged_s32h32_d128.json")
+GQA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_paged_s32h32kv8_d128.json")
 
 
 def attention_flops(B, H, Nq, Nk, d, causal):
@@ -53,11 +58,13 @@ def attention_flops(B, H, Nq, Nk, d, causal):
     return f * 0.5 if causal else f
 
 
-def decode_bytes(kv_lens, H, d, elem=2, with_io=True):
-    """Algorithmic bytes of one decode call: every cached K and V element once,
-    plus q, o (fp32), lse (fp32), the page-table entries used and kv_lens."""
+def decode_bytes(kv_lens, H, d, elem=2, with_io=True, Hkv=None):
+    """Algorithmic bytes of one decode call: every cached K and V element once
+    (Hkv heads of them), plus q, o (fp32), lse (fp32) of the H query heads, the
+    page-table entries used and kv_lens."""
+    Hkv = H if Hkv is None else Hkv
     tokens = int(np.sum(kv_lens))
-    b = 2 * tokens * H * d * elem
+    b = 2 * tokens * Hkv * d * elem
     if with_io:
         S = len(kv_lens)
         pages = int(np.sum((np.asarray(kv_lens) + 15) // 16))
@@ -110,8 +117,10 @@ def record_traffic(d, copy_bytes):
     """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
     this benchmark and of a plain copy of copy_bytes into bytes per launch:
     each counter is scaled by (bytes the copy moves) / (what it reads for the
-    copy).  Expects run dirs <d>/{fwd,copy}_{FETCH_SIZE,WRITE_SIZE}/ holding
-    run_counter_collection.csv (see the profile notes for the commands)."""
+    copy).  Expects run dirs <d>/{fwd,gqa,copy}_{FETCH_SIZE,WRITE_SIZE}/ holding
+    run_counter_collection.csv: fwd_* from a run with --no-gqa (forward and
+    decode), gqa_* from a run with --gqa-only (see the profile notes for the
+    commands)."""
     def one(sub, counter):
         return _counter_means(os.path.join(d, sub, "run_counter_collection.csv"), counter)
 
@@ -120,13 +129,16 @@ def record_traffic(d, copy_bytes):
         copy = [v for k, v in one("copy_" + c, c).items() if "copyBuffer" in k]
         factor[c] = copy_bytes / (copy[0] * 1024.0)
     out = {}
-    for label, match, path, sources in (
-            ("fwd", "fwd_kernel", TRAFFIC_FILE, ("fa_fwd.hip", "fa_common.h")),
-            ("decode", "decode_", DEC_TRAFFIC_FILE, DEC_SOURCES)):
+    for label, run, match, path, sources in (
+            ("fwd", "fwd_", "fwd_kernel", TRAFFIC_FILE, ("fa_fwd.hip", "fa_common.h")),
+            ("decode", "fwd_", "decode_", DEC_TRAFFIC_FILE, DEC_SOURCES),
+            ("decode_gqa", "gqa_", "decode_", GQA_TRAFFIC_FILE, DEC_SOURCES)):
+        if not os.path.isdir(os.path.join(d, run + "FETCH_SIZE")):
+            continue
         rec = {"kernel_digest": kernel_digest(sources), "calibration": factor}
         total = 0.0
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            kib = sum(v for k, v in one("fwd_" + c, c).items() if match in k)
+            kib = sum(v for k, v in one(run + c, c).items() if match in k)
             rec[c + "_KiB_raw"] = kib
             rec[c + "_bytes"] = kib * 1024.0 * factor[c]
             total += rec[c + "_bytes"]
@@ -199,6 +211,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="time the forward only")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode")
+    ap.add_argument("--gqa-only", action="store_true",
+                    help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter "
                          "calibration for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -230,6 +245,18 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
         return
+    if args.gqa_only:
+        gq = gen.decode_workload(GQA_WORKLOAD)
+        pools = (gen.build_pool_device(gq, "k", dev), gen.build_pool_device(gq, "v", dev))
+        g_q = gen.to_torch(gq.q, gq.dtype).to(dev)
+        g_pt = torch.from_numpy(gq.page_table).to(dev)
+        g_kl = torch.from_numpy(gq.kv_lens).to(dev)
+        for _ in range(args.warmup + args.steps):
+            fa.decode_paged(g_q, *pools, g_pt, g_kl, scale=gq.scale)
+        torch.cuda.synchronize()
+        print(json.dumps({"gqa_only": GQA_WORKLOAD, "launches": args.warmup + args.steps}),
+              flush=True)
+        return
 
     print(f"[bench] generating {FWD_WORKLOAD}", file=sys.stderr, flush=True)
     w = gen.fwd_workload(FWD_WORKLOAD)
@@ -254,6 +281,21 @@ def main():
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         dbytes = decode_bytes(dec.kv_lens, dec.H, dec.d)
 
+    gq = None
+    if not args.no_decode and not args.no_gqa:
+        print(f"[bench] generating {GQA_WORKLOAD}", file=sys.stderr, flush=True)
+        gq = gen.decode_workload(GQA_WORKLOAD)
+        g_kp = gen.build_pool_device(gq, "k", dev)
+        g_vp = gen.build_pool_device(gq, "v", dev)
+        g_q = gen.to_torch(gq.q, gq.dtype).to(dev)
+        g_pt = torch.from_numpy(gq.page_table).to(dev)
+        g_kl = torch.from_numpy(gq.kv_lens).to(dev)
+        g_o = torch.empty((gq.S, gq.H, gq.d), dtype=torch.float32, device=dev)
+        g_lse = torch.empty((gq.S, gq.H), dtype=torch.float32, device=dev)
+        g_wsb = fa.fa_decode_workspace_bytes(gq.S, gq.H, gq.d, gq.page_table.shape[1], 16)
+        g_ws = torch.empty(max(g_wsb, 16), dtype=torch.uint8, device=dev)
+        gbytes = decode_bytes(gq.kv_lens, gq.H, gq.d, Hkv=gq.Hkv)
+
     def step(evs=None):
         if evs is not None:
             evs[0].record()
@@ -264,13 +306,18 @@ def main():
             fa.decode_paged(dq, kp, vp, dpt, dkl, scale=dec.scale, workspace=ws, out=(do, dlse))
             if evs is not None:
                 evs[2].record()
+        if gq is not None:
+            fa.decode_paged(g_q, g_kp, g_vp, g_pt, g_kl, scale=gq.scale, workspace=g_ws,
+                            out=(g_o, g_lse))
+            if evs is not None:
+                evs[3].record()
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print("[bench] timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -296,7 +343,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": FWD_WORKLOAD, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d,
-                   "causal": True, "decode_workload": None if dec is None else DEC_WORKLOAD},
+                   "causal": True, "decode_workload": None if dec is None else DEC_WORKLOAD,
+                   "decode_gqa_workload": None if gq is None else GQA_WORKLOAD},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic()},
@@ -315,6 +363,18 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic(DEC_TRAFFIC_FILE, DEC_SOURCES)},
+        }
+    if gq is not None:
+        g_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+        g_gbs = gbytes / (float(g_ms.mean()) / 1e3) / 1e9
+        result["decode_gqa"] = {
+            "GB/s": g_gbs, "kernel_ms_avg": float(g_ms.mean()),
+            "kernel_ms_p10": float(np.percentile(g_ms, 10)),
+            "kernel_ms_p90": float(np.percentile(g_ms, 90)),
+            "bytes": gbytes, "tokens": int(gq.kv_lens.sum()), "H": gq.H, "H_kv": gq.Hkv,
+            "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": g_gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(GQA_TRAFFIC_FILE, DEC_SOURCES)},
         }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

@@ -276,12 +276,20 @@ FWD_WORKLOADS = {
     "fwd_padded_b8h16_n2048_d64_bf16": dict(B=8, H=16, Nq=2048, Nk=2048, d=64,
                                             dtype="bf16", causal=False, scale=0.125,
                                             kv_len_range=(1024, 2048), seed=4000),
+    # grouped-query heads: 16 query heads over 4 K/V heads
+    "fwd_causal_b8h16kv4_n4096_d64_bf16": dict(B=8, H=16, Hkv=4, Nq=4096, Nk=4096, d=64,
+                                               dtype="bf16", causal=True, scale=0.125,
+                                               seed=3004),
 }
 
 DECODE_WORKLOADS = {
     "decode_paged_s32h32_d128_bf16": dict(S=32, H=32, d=128, len_range=(512, 8192),
                                           dtype="bf16", page_size=16, num_pages=1 << 16,
                                           scale=1.0 / math.sqrt(128), seed=5000),
+    # the same batch with grouped-query heads: 32 query heads over 8 K/V heads
+    "decode_paged_s32h32kv8_d128_bf16": dict(S=32, H=32, Hkv=8, d=128, len_range=(512, 8192),
+                                             dtype="bf16", page_size=16, num_pages=1 << 16,
+                                             scale=1.0 / math.sqrt(128), seed=5001),
 }
 
 

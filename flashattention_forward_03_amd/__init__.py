@@ -6,12 +6,15 @@ device memory and the current stream.  There is no CPU path: if the library
 is missing or no GPU is present, calls raise.
 
 Two layers:
-  * ``fa_fwd``, ``fa_decode_paged``, ``fa_decode_workspace_bytes``,
-    ``fa_status_str``, ``fa_last_hip_error``: the C entry points with the same
-    names and arguments (raw device addresses as ints, stream as int).
+  * ``fa_fwd``, ``fa_fwd_gqa``, ``fa_decode_paged``, ``fa_decode_paged_gqa``,
+    ``fa_decode_workspace_bytes``, ``fa_status_str``, ``fa_last_hip_error``:
+    the C entry points with the same names and arguments (raw device
+    addresses as ints, stream as int).
   * ``forward`` / ``decode_paged``: take torch tensors, check them, allocate
     the outputs (and the decode workspace), call the entry point on the
-    current stream and raise ``FAError`` on a non-zero status.
+    current stream and raise ``FAError`` on a non-zero status.  The number
+    of K/V heads is read from k (or the pools); fewer K/V heads than query
+    heads go to the ``_gqa`` entry point.
 """
 from __future__ import annotations
 
@@ -34,8 +37,8 @@ FA_ERR_ARG = 7
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 
-EXPORTED = ("fa_fwd", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_str",
-            "fa_last_hip_error", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_decode_paged", "fa_decode_paged_gqa",
+            "fa_decode_workspace_bytes", "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -81,8 +84,12 @@ def load_library():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P]
     lib.fa_fwd.restype = I
+    lib.fa_fwd_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    lib.fa_fwd_gqa.restype = I
     lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode_paged.restype = I
+    lib.fa_decode_paged_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fa_decode_paged_gqa.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_decode_workspace_bytes.restype = Z
     lib.fa_status_str.argtypes = [I]
@@ -102,12 +109,27 @@ def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_lens, dtype, stre
                                  stream)
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, kv_lens, dtype,
+               stream) -> int:
+    return load_library().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal,
+                                     kv_lens, dtype, stream)
+
+
 def fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
                     max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes,
                     stream) -> int:
     return load_library().fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H,
                                           d, page_size, max_pages_per_seq, num_pages, scale,
                                           dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H_kv, d,
+                        page_size, max_pages_per_seq, num_pages, scale, dtype, workspace,
+                        workspace_bytes, stream) -> int:
+    return load_library().fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse,
+                                              S, H, H_kv, d, page_size, max_pages_per_seq,
+                                              num_pages, scale, dtype, workspace,
+                                              workspace_bytes, stream)
 
 
 def fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size) -> int:
@@ -154,20 +176,23 @@ def _stream_handle(stream) -> int:
 
 def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
             kv_lens=None, stream=None, out=None):
-    """Exact attention forward on [B, H, N, d] f16/bf16 tensors.
+    """Exact attention forward: q [B, H, Nq, d], k/v [B, H_kv, Nk, d] f16/bf16
+    (H a multiple of H_kv; query head h reads K/V head h // (H // H_kv)).
 
     Returns ``(o, lse)``: o float32 [B, H, Nq, d], lse float32 [B, H, Nq].
     ``kv_lens``: optional int32 GPU tensor [B] of valid key counts.
     """
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, d) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the query heads must be a multiple of the K/V heads")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t)
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -184,25 +209,33 @@ def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
-                Nk, d, float(scale), int(bool(causal)), kl_ptr, dt, _stream_handle(stream))
+    if Hkv == H:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                    Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt, _stream_handle(stream))
+    else:
+        st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B,
+                        H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt,
+                        _stream_handle(stream))
     if st != FA_OK:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, "fa_fwd" if Hkv == H else "fa_fwd_gqa")
     return o, lse
 
 
 def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[float] = None,
                  workspace=None, stream=None, out=None):
-    """Decode attention: q [S, H, d], pools [num_pages, H, page_size, d],
-    page_table int32 [S, max_pages], kv_lens int32 [S].  Returns (o, lse)."""
+    """Decode attention: q [S, H, d], pools [num_pages, H_kv, page_size, d] (H a
+    multiple of H_kv), page_table int32 [S, max_pages], kv_lens int32 [S].
+    Returns (o, lse)."""
     torch = _torch()
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
                     ("page_table", page_table), ("kv_lens", kv_lens)):
         _check_dev(name, t)
     S, H, d = q.shape
-    num_pages, Hp, page_size, dp = k_pages.shape
-    if (Hp, dp) != (H, d) or v_pages.shape != k_pages.shape:
-        raise ValueError("pools must be [num_pages, H, page_size, d] matching q")
+    num_pages, Hkv, page_size, dp = k_pages.shape
+    if dp != d or v_pages.shape != k_pages.shape:
+        raise ValueError("pools must be [num_pages, H_kv, page_size, d] matching q")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the query heads must be a multiple of the K/V heads")
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != S:
         raise ValueError("page_table must be int32 [S, max_pages]")
     if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (S,):
@@ -223,10 +256,16 @@ def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[fl
         lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    st = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                         page_table.data_ptr(), kv_lens.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         S, H, d, page_size, max_pages, num_pages, float(scale), dt, ws_ptr,
-                         ws_bytes, _stream_handle(stream))
+    if Hkv == H:
+        st = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                             page_table.data_ptr(), kv_lens.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), S, H, d, page_size, max_pages, num_pages,
+                             float(scale), dt, ws_ptr, ws_bytes, _stream_handle(stream))
+    else:
+        st = fa_decode_paged_gqa(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                 page_table.data_ptr(), kv_lens.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), S, H, Hkv, d, page_size, max_pages, num_pages,
+                                 float(scale), dt, ws_ptr, ws_bytes, _stream_handle(stream))
     if st != FA_OK:
-        raise FAError(st, "fa_decode_paged")
+        raise FAError(st, "fa_decode_paged" if Hkv == H else "fa_decode_paged_gqa")
     return o, lse

@@ -64,10 +64,12 @@ const char *fa_status_str(int status)
 
 int fa_last_hip_error(void) { return g_last_hip_error; }
 
-int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int Nq,
-           int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv,
+               int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
 {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+        return FA_ERR_SHAPE;
+    if (H > 0 && (H_kv < 1 || H % H_kv != 0))
         return FA_ERR_SHAPE;
     if (d != 64 && d != 128)
         return FA_ERR_UNSUPPORTED;
@@ -89,11 +91,17 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
         !aligned(kv_lens, 4))
         return FA_ERR_ALIGN;
 
-    fa::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal == 1, dtype == FA_DTYPE_BF16, kv_lens};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal == 1, dtype == FA_DTYPE_BF16, kv_lens};
     const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "fa_fwd launch");
     return FA_OK;
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int Nq,
+           int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+{
+    return fa_fwd_gqa(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, kv_lens, dtype, stream);
 }
 
 size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size)
@@ -103,12 +111,14 @@ size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int
     return decode_ws_bytes(S, H, d, max_pages_per_seq);
 }
 
-int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
-                    const int32_t *kv_lens, float *o, float *lse, int S, int H, int d, int page_size,
-                    int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
-                    size_t workspace_bytes, void *stream)
+int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                        const int32_t *kv_lens, float *o, float *lse, int S, int H, int H_kv, int d, int page_size,
+                        int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
+                        size_t workspace_bytes, void *stream)
 {
     if (S < 0 || H < 0 || max_pages_per_seq < 1 || num_pages < 1)
+        return FA_ERR_SHAPE;
+    if (H > 0 && (H_kv < 1 || H % H_kv != 0))
         return FA_ERR_SHAPE;
     if (d != 64 && d != 128)
         return FA_ERR_UNSUPPORTED;
@@ -140,12 +150,21 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
     float *part_o = need ? static_cast<float *>(workspace) : nullptr;
     float *part_ml = need ? part_o + (size_t)S * H * chunks * d : nullptr;
 
-    fa::DecodeArgs a{q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
+    fa::DecodeArgs a{q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H_kv, d, page_size,
                      max_pages_per_seq, num_pages, scale, dtype == FA_DTYPE_BF16, part_o, part_ml};
     const hipError_t e = fa::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "fa_decode_paged launch");
     return FA_OK;
+}
+
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                    const int32_t *kv_lens, float *o, float *lse, int S, int H, int d, int page_size,
+                    int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    return fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H, d, page_size,
+                               max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

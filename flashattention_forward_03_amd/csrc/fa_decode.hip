@@ -68,29 +68,72 @@ __device__ __forceinline__ void widen8(const u32x4_t &w, float *f)
     }
 }
 
-template <int D, bool BF16>
+// Dot product of 8 packed head dims (two per dword): products are exact in
+// fp32 (8- or 11-bit significands), sums rounded to fp32.  The dwords are
+// copied out of the vectors before the bit casts: a bit cast applied to a
+// vector element directly was compiled to read element 0 every time.
+template <bool BF16>
+__device__ __forceinline__ float dot8(const u32x4_t &a, const u32x4_t &b)
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ai = a[i], bi = b[i];
+        if constexpr (BF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ai), __builtin_bit_cast(bf16x2_t, bi),
+                                                  acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ai), __builtin_bit_cast(f16x2_t, bi), acc, false);
+    }
+    return acc;
+}
+
+// Sum / max over the token rows of a wave: lanes that differ only in the
+// bits above log2(TPR) (the same 8 head dims of different rows).
+template <int TPR>
+__device__ __forceinline__ float rows_sum(float x)
+{
+    if constexpr (TPR == 8)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // lane ^ 8
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));                          // lane ^ 16
+    return x + other_half(x);                                                                            // lane ^ 32
+}
+template <int TPR>
+__device__ __forceinline__ float rows_max(float x)
+{
+    if constexpr (TPR == 8)
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
+    return fmaxf(x, other_half(x));
+}
+
+// Split-KV pass.  Work item of one wave: (sequence, chunk, K/V head, slice of
+// up to QPW of the query heads that read that K/V head).  Every K/V row the
+// wave loads serves all QPW query heads, so grouped-query heads cost no
+// extra K/V traffic.
+template <int D, bool BF16, int QPW>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
     const uint16_t *__restrict__ Qp, const uint16_t *__restrict__ Kp, const uint16_t *__restrict__ Vp,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ kv_lens, float *__restrict__ O,
-    float *__restrict__ LSE, float *__restrict__ part_o, float *__restrict__ part_ml, int H, int n_hgroups,
-    int max_pages, int num_pages, int max_chunks, float c_log2)
+    float *__restrict__ LSE, float *__restrict__ part_o, float *__restrict__ part_ml, int H, int Hkv, int group,
+    int n_slices, int n_items, int n_wgroups, int max_pages, int num_pages, int max_chunks, float c_log2)
 {
     constexpr int TPR = D / 8;              // lanes per token row (8 head dims each)
     constexpr int RPW = 64 / TPR;           // token rows per wave step (4 or 8)
     constexpr int SPP = PAGE / RPW;         // wave steps per page (4 or 2)
     constexpr int CHUNK = kDecodeChunkPages;
-    constexpr int DPL = D / 64;             // head dims per lane in the final merge
-
-    __shared__ float sm_m[GROUP][RPW], sm_l[GROUP][RPW];
-    __shared__ float sm_o[GROUP][RPW][D + 4];
+    constexpr int SIF = QPW <= 2 ? STEPS_IN_FLIGHT : (QPW == 4 ? STEPS_IN_FLIGHT / 2 : STEPS_IN_FLIGHT / 4);
 
     const int chunk = blockIdx.x % max_chunks;
-    const int shg = blockIdx.x / max_chunks;
-    const int s = shg / n_hgroups, hg = shg - s * n_hgroups;
+    const int swg = blockIdx.x / max_chunks;
+    const int s = swg / n_wgroups, wg = swg - s * n_wgroups;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = hg * GROUP + wave;
-    const bool head_ok = h < H;
+    const int item = wg * GROUP + wave;
+    const bool item_ok = item < n_items;
+    const int kvh = item_ok ? item / n_slices : 0;
+    const int h0 = kvh * group + (item_ok ? item - kvh * n_slices : 0) * QPW;   // first query head
+    const int nq = item_ok ? min(QPW, kvh * group + group - h0) : 0;          // query heads in the slice
 
     int kvlen = kv_lens[s];
     kvlen = kvlen < 0 ? 0 : (kvlen > max_pages * PAGE ? max_pages * PAGE : kvlen);
@@ -100,22 +143,25 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
         return;
     const int p_begin = chunk * CHUNK;
     const int p_end = min(p_begin + CHUNK, npages);
-    const int nsteps = head_ok ? (p_end - p_begin) * SPP : 0;
+    const int nsteps = nq > 0 ? (p_end - p_begin) * SPP : 0;
 
     const int r = lane / TPR;      // token row within a wave step
     const int gd = lane - r * TPR; // which 8 head dims
-    const size_t sh = (size_t)s * H + (head_ok ? h : 0);
 
-    float qv[8];
-    widen8<BF16>(load16(Qp + sh * D + 8 * gd), qv);
+    u32x4_t qv[QPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        qv[i] *= c_log2;
+    for (int j = 0; j < QPW; ++j)
+        qv[j] = load16(Qp + ((size_t)s * H + h0 + min(j, max(nq - 1, 0))) * D + 8 * gd);
 
-    float m = -INFINITY, l = 0.f, acc[8];
+    float m[QPW], l[QPW], acc[QPW][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        acc[i] = 0.f;
+    for (int j = 0; j < QPW; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[j][i] = 0.f;
+    }
 
     // the chunk's physical page ids, one per lane (CHUNK <= 64), read once so
     // that the K/V loads of each step do not wait behind a page-table load
@@ -125,14 +171,14 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
         phys_lane = page_table[(size_t)s * max_pages + p_begin + lane];
         phys_lane = phys_lane < 0 ? 0 : (phys_lane >= num_pages ? num_pages - 1 : phys_lane);
     }
-    const size_t head_off = (size_t)(head_ok ? h : 0) * PAGE * D + 8 * gd;
-    const size_t page_stride = (size_t)H * PAGE * D;
+    const size_t head_off = (size_t)kvh * PAGE * D + 8 * gd;
+    const size_t page_stride = (size_t)Hkv * PAGE * D;
 
-    for (int k0 = 0; k0 < nsteps; k0 += STEPS_IN_FLIGHT) {
-        u32x4_t kr[STEPS_IN_FLIGHT], vr[STEPS_IN_FLIGHT];
-        bool ok[STEPS_IN_FLIGHT];
+    for (int k0 = 0; k0 < nsteps; k0 += SIF) {
+        u32x4_t kr[SIF], vr[SIF];
+        bool ok[SIF];
 #pragma unroll
-        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
+        for (int u = 0; u < SIF; ++u) {
             const int step = k0 + u;
             const int page = p_begin + step / SPP;
             const int row = (step % SPP) * RPW + r;
@@ -148,82 +194,78 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(
                 vr[u] = u32x4_t{0, 0, 0, 0};
             }
         }
-        float t[STEPS_IN_FLIGHT];
-        float mx = -INFINITY;
+        // base-2 scores of every query head, then one rescale per head
+        float t[QPW][SIF], mref[QPW];
 #pragma unroll
-        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
-            float kf[8];
-            widen8<BF16>(kr[u], kf);
-            float dot = 0.f;
+        for (int j = 0; j < QPW; ++j) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < SIF; ++u) {
+                float dot = dot8<BF16>(qv[j], kr[u]);
+                dot = (TPR == 16) ? row16_sum(dot) : row8_sum(dot);
+                t[j][u] = ok[u] ? dot * c_log2 : -INFINITY;
+                mx = fmaxf(mx, t[j][u]);
+            }
+            const float m_new = fmaxf(m[j], mx);
+            mref[j] = m_new == -INFINITY ? 0.f : m_new;   // rows with no valid token yet stay at zero
+            const float alpha = fast_exp2(m[j] - mref[j]);
+            l[j] *= alpha;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                dot = fmaf(qv[i], kf[i], dot);
-            dot = (TPR == 16) ? row16_sum(dot) : row8_sum(dot);
-            t[u] = ok[u] ? dot : -INFINITY;
-            mx = fmaxf(mx, t[u]);
+                acc[j][i] *= alpha;
+            m[j] = m_new;
         }
-        const float m_new = fmaxf(m, mx);
-        if (m_new == -INFINITY)
-            continue;
-        const float alpha = fast_exp2(m - m_new);
-        l *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] *= alpha;
-#pragma unroll
-        for (int u = 0; u < STEPS_IN_FLIGHT; ++u) {
-            const float p = fast_exp2(t[u] - m_new);
-            l += p;
+        for (int u = 0; u < SIF; ++u) {
             float vf[8];
             widen8<BF16>(vr[u], vf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i] = fmaf(p, vf[i], acc[i]);
+            for (int j = 0; j < QPW; ++j) {
+                const float p = fast_exp2(t[j][u] - mref[j]);
+                l[j] += p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[j][i] = fmaf(p, vf[i], acc[j][i]);
+            }
         }
-        m = m_new;
     }
 
-    // ---- merge the RPW token streams of each wave's head (log-sum-exp rule)
-    if (gd == 0) {
-        sm_m[wave][r] = m;
-        sm_l[wave][r] = l;
-    }
+    // ---- merge the RPW token streams of each head (log-sum-exp rule); the
+    // lanes of row 0 write the chunk's result, 8 head dims each
+    const bool writer = r == 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        sm_o[wave][r][8 * gd + i] = acc[i];
-    __syncthreads();
-    if (!head_ok)
-        return;
-    float M = -INFINITY;
+    for (int j = 0; j < QPW; ++j) {
+        if (j >= nq)
+            break;
+        const float M = rows_max<TPR>(m[j]);
+        const float w = m[j] == -INFINITY ? 0.f : fast_exp2(m[j] - M);
+        const float L = rows_sum<TPR>(w * l[j]);
+        float o[8];
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
-        M = fmaxf(M, sm_m[wave][j]);
-    float w[RPW];
-    float L = 0.f;
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        w[j] = sm_m[wave][j] == -INFINITY ? 0.f : fast_exp2(sm_m[wave][j] - M);
-        L = fmaf(w[j], sm_l[wave][j], L);
-    }
-    const size_t slot = sh * max_chunks + chunk;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-        const int dim = lane + 64 * k;
-        float num = 0.f;
-#pragma unroll
-        for (int j = 0; j < RPW; ++j)
-            num = fmaf(w[j], sm_o[wave][j][dim], num);
-        if (nchunks == 1)
-            O[sh * D + dim] = num / L;
-        else
-            part_o[slot * D + dim] = num;
-    }
-    if (lane == 0) {
+        for (int i = 0; i < 8; ++i)
+            o[i] = rows_sum<TPR>(w * acc[j][i]);
+        const size_t sh = (size_t)s * H + h0 + j;
+        float *dst;
+        float sc;
         if (nchunks == 1) {
-            LSE[sh] = (M + __log2f(L)) * kLn2;
+            dst = O + sh * D;
+            sc = 1.f / L;
         } else {
-            part_ml[2 * slot] = M;
-            part_ml[2 * slot + 1] = L;
+            dst = part_o + (sh * max_chunks + chunk) * D;
+            sc = 1.f;
+        }
+        if (writer) {
+            *reinterpret_cast<f32x4_t *>(dst + 8 * gd) = f32x4_t{o[0] * sc, o[1] * sc, o[2] * sc, o[3] * sc};
+            *reinterpret_cast<f32x4_t *>(dst + 8 * gd + 4) = f32x4_t{o[4] * sc, o[5] * sc, o[6] * sc, o[7] * sc};
+        }
+        if (lane == 0) {
+            if (nchunks == 1) {
+                LSE[sh] = (M + __log2f(L)) * kLn2;
+            } else {
+                const size_t slot = sh * max_chunks + chunk;
+                part_ml[2 * slot] = M;
+                part_ml[2 * slot + 1] = L;
+            }
         }
     }
 }
@@ -323,22 +365,41 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const int32_t 
         LSE[sh] = (M + __log2f(L)) * kLn2;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int QPW>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 {
     const int max_chunks = decode_max_chunks(a.max_pages);
-    const int n_hgroups = (a.H + GROUP - 1) / GROUP;
-    const long long grid = (long long)a.S * n_hgroups * max_chunks;
-    hipLaunchKernelGGL((decode_split_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
+    const int group = a.H / a.Hkv;
+    const int n_slices = (group + QPW - 1) / QPW;
+    const int n_items = a.Hkv * n_slices;
+    const int n_wgroups = (n_items + GROUP - 1) / GROUP;
+    const long long grid = (long long)a.S * n_wgroups * max_chunks;
+    hipLaunchKernelGGL((decode_split_kernel<D, BF16, QPW>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k_pages, (const uint16_t *)a.v_pages,
-                       a.page_table, a.kv_lens, a.o, a.lse, a.part_o, a.part_ml, a.H, n_hgroups, a.max_pages,
-                       a.num_pages, max_chunks, a.scale * kLog2e);
+                       a.page_table, a.kv_lens, a.o, a.lse, a.part_o, a.part_ml, a.H, a.Hkv, group, n_slices,
+                       n_items, n_wgroups, a.max_pages, a.num_pages, max_chunks, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    const int n_hgroups = (a.H + GROUP - 1) / GROUP;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.S * n_hgroups)), dim3(NTHREADS), 0, stream,
                        a.kv_lens, a.part_o, a.part_ml, a.o, a.lse, a.H, n_hgroups, a.max_pages, max_chunks);
     return hipGetLastError();
+}
+
+// Query heads per wave: the whole group when it has at most 8 heads (padded
+// to 1, 2, 4 or 8), else slices of 8.
+template <int D, bool BF16>
+hipError_t launch_qpw(const DecodeArgs &a, hipStream_t stream)
+{
+    const int group = a.H / a.Hkv;
+    if (group == 1)
+        return launch<D, BF16, 1>(a, stream);
+    if (group == 2)
+        return launch<D, BF16, 2>(a, stream);
+    if (group <= 4)
+        return launch<D, BF16, 4>(a, stream);
+    return launch<D, BF16, 8>(a, stream);
 }
 
 }  // namespace
@@ -346,8 +407,8 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.d == 64)
-        return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
-    return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+        return a.bf16 ? launch_qpw<64, true>(a, stream) : launch_qpw<64, false>(a, stream);
+    return a.bf16 ? launch_qpw<128, true>(a, stream) : launch_qpw<128, false>(a, stream);
 }
 
 }  // namespace fa

@@ -466,14 +466,16 @@ __device__ __forceinline__ void attend_qtile(
 // qt = n_qtiles-1 - blockIdx / (B*H), so the heaviest tiles (most key tiles)
 // are dispatched first and the dispatcher fills the GPU longest job first;
 // the light diagonal-corner tiles form the tail.  blockIdx % (B*H) picks the
-// head, and since workgroups go to XCD blockIdx % 8, all tiles of one head
-// share an XCD (and its L2) whenever B*H is a multiple of 8.  Non-causal:
-// work ids are renumbered so that each XCD receives a contiguous range.
+// head; workgroups go to XCD blockIdx % 8, and when B*H is a multiple of 8
+// the heads are renumbered so that each XCD holds a contiguous range of them:
+// all tiles of a head, and the query heads that share a K/V head, then share
+// one XCD and its L2.  Non-causal: work ids are renumbered so that each XCD
+// receives a contiguous range.
 // The causal flag is a runtime argument: both modes share one code path.
 template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ LSE, int H, int Nq, int Nk, int n_qtiles, int n_units,
+    float *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk, int n_qtiles, int n_units,
     float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
@@ -496,11 +498,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
 
     int bhi, qt;
     if (causal) {
-        // one query tile per workgroup, heaviest tiles first, so the dispatcher
-        // fills the GPU longest job first; blockIdx % (B*H) picks the head, so
-        // with B*H a multiple of 8 all tiles of a head share one XCD
         const int BHn = gridDim.x / n_qtiles;
-        bhi = blockIdx.x % BHn;
+        const int slot = blockIdx.x % BHn;
+        bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);
         qt = n_qtiles - 1 - blockIdx.x / BHn;
     } else {
         const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -509,13 +509,14 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
     }
     const size_t bh = (size_t)bhi;
     const int b = bhi / H;
+    const size_t kvh = (size_t)b * Hkv + (bhi - b * H) / (H / Hkv);   // K/V head of this query head
     int kvlen = Nk;
     if (kv_lens) {
         kvlen = kv_lens[b];
         kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
     }
-    const uint16_t *Kb = K + bh * Nk * D;
-    const uint16_t *Vb = V + bh * Nk * D;
+    const uint16_t *Kb = K + kvh * Nk * D;
+    const uint16_t *Vb = V + kvh * Nk * D;
 
     attend_qtile<D, BF16>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal, kbuf, vbuf,
                           wave, lane);
@@ -536,7 +537,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     const long long grid = (long long)n_units * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
-                       a.H, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.causal ? 1 : 0,
+                       a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.causal ? 1 : 0,
                        a.kv_lens);
     return hipGetLastError();
 }

@@ -10,7 +10,7 @@ namespace fa {
 struct FwdArgs {
     const void *q, *k, *v;
     float *o, *lse;
-    int B, H, Nq, Nk, d;
+    int B, H, Hkv, Nq, Nk, d;   // query head h reads K/V head h / (H / Hkv)
     float scale;
     bool causal, bf16;
     const int32_t *kv_lens;
@@ -20,7 +20,7 @@ struct DecodeArgs {
     const void *q, *k_pages, *v_pages;
     const int32_t *page_table, *kv_lens;
     float *o, *lse;
-    int S, H, d, page_size, max_pages, num_pages;
+    int S, H, Hkv, d, page_size, max_pages, num_pages;   // query head h reads K/V head h / (H / Hkv)
     float scale;
     bool bf16;
     float *part_o, *part_ml;   // workspace views (NULL when one chunk covers every sequence)

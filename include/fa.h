@@ -95,6 +95,21 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
            void *stream);
 
 /*
+ * fa_fwd with grouped-query heads (multi-query and grouped-query attention,
+ * the head-sharing variants of the llm-kernel-lib page's "Ablation Study"):
+ *
+ *   k, v     [B, H_kv, Nk, d]; H must be a positive multiple of H_kv.  Query
+ *            head h reads K/V head h / (H / H_kv): consecutive query heads
+ *            share one K/V head.  H_kv = H is fa_fwd; H_kv = 1 is multi-query.
+ *
+ * Every other argument, layout, alignment and error as for fa_fwd; H_kv < 1
+ * or H not a multiple of H_kv (with H > 0) is FA_ERR_SHAPE.
+ */
+int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
+               int H_kv, int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens,
+               int dtype, void *stream);
+
+/*
  * Decode attention over a paged KV cache (query length 1).
  *
  *   q           [S, H, d] f16/bf16; 16-byte aligned
@@ -127,6 +142,24 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int S, int H, int d, int page_size, int max_pages_per_seq, int num_pages,
                     float scale, int dtype, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * fa_decode_paged with grouped-query heads (see fa_fwd_gqa):
+ *
+ *   k_pages,
+ *   v_pages     [num_pages, H_kv, page_size, d]; H a positive multiple of H_kv.
+ *               Query head h reads K/V head h / (H / H_kv).
+ *
+ * The K/V rows of a page are read once for all the query heads that share
+ * them.  Workspace: fa_decode_workspace_bytes(S, H, ...) with H the number of
+ * QUERY heads.  Every other argument and error as for fa_decode_paged; H_kv < 1
+ * or H not a multiple of H_kv (with H > 0) is FA_ERR_SHAPE.
+ */
+int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages,
+                        const int32_t *page_table, const int32_t *kv_lens, float *o, float *lse,
+                        int S, int H, int H_kv, int d, int page_size, int max_pages_per_seq,
+                        int num_pages, float scale, int dtype, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* Workspace bytes fa_decode_paged needs for these sizes (0 for invalid sizes). */
 size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size);

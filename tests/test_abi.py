@@ -87,6 +87,30 @@ def test_fwd_argument_checks(lib, over, status):
     assert call_fwd(**over) == status
 
 
+def call_fwd_gqa(H_kv, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.fa_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], H_kv, a["Nq"],
+                         a["Nk"], a["d"], a["scale"], a["causal"], a["kv_lens"], a["dtype"],
+                         a["stream"])
+
+
+@pytest.mark.parametrize("H,H_kv,over,status", [
+    (4, 0, {}, fa.FA_ERR_SHAPE),
+    (4, -2, {}, fa.FA_ERR_SHAPE),
+    (4, 3, {}, fa.FA_ERR_SHAPE),        # 4 query heads cannot share 3 K/V heads evenly
+    (4, 8, {}, fa.FA_ERR_SHAPE),        # more K/V heads than query heads
+    (6, 4, {}, fa.FA_ERR_SHAPE),
+    (0, 0, dict(q=None, o=None, lse=None), fa.FA_OK),   # no query head: empty problem
+    (4, 2, dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (4, 2, dict(k=None), fa.FA_ERR_NULL),
+    (4, 1, dict(v=A + 2), fa.FA_ERR_ALIGN),
+    (4, 2, dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
+])
+def test_fwd_gqa_argument_checks(lib, H, H_kv, over, status):
+    assert call_fwd_gqa(H_kv, H=H, **over) == status
+
+
 GOOD_DEC = dict(q=A, kp=A, vp=A, pt=A, kl=A, o=A, lse=A, S=2, H=2, d=128, page_size=16,
                 max_pages=100, num_pages=64, scale=0.088, dtype=1, ws=A, ws_bytes=1 << 30,
                 stream=None)
@@ -148,3 +172,37 @@ def test_binding_keeps_one_hip_runtime_in_the_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True)
     assert out.stdout.strip() == "1"
+
+
+def call_dec_gqa(H_kv, **over):
+    a = dict(GOOD_DEC)
+    a.update(over)
+    return fa.fa_decode_paged_gqa(a["q"], a["kp"], a["vp"], a["pt"], a["kl"], a["o"], a["lse"],
+                                  a["S"], a["H"], H_kv, a["d"], a["page_size"], a["max_pages"],
+                                  a["num_pages"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("H,H_kv,over,status", [
+    (8, 0, {}, fa.FA_ERR_SHAPE),
+    (8, 3, {}, fa.FA_ERR_SHAPE),
+    (8, 16, {}, fa.FA_ERR_SHAPE),
+    (8, -1, {}, fa.FA_ERR_SHAPE),
+    (0, 0, dict(q=None, o=None), fa.FA_OK),
+    (8, 2, dict(page_size=32), fa.FA_ERR_UNSUPPORTED),
+    (8, 2, dict(kp=None), fa.FA_ERR_NULL),
+    (8, 1, dict(ws=None), fa.FA_ERR_WORKSPACE),
+    # the workspace is sized by the QUERY heads: 8 heads x 7 chunks
+    (8, 2, dict(ws_bytes=2 * 8 * 7 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_gqa_argument_checks(lib, H, H_kv, over, status):
+    assert call_dec_gqa(H_kv, H=H, **over) == status
+
+
+def test_binding_checks_head_grouping(lib):
+    import torch
+
+    q = torch.zeros(1, 6, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="multiple of the K/V heads"):
+        fa.forward(q, k, k)

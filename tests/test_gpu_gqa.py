@@ -1,0 +1,153 @@
+"""GPU parity of the grouped-query entry points (fa_fwd_gqa, fa_decode_paged_gqa)
+against the fp64 oracle, through the C ABI binding.  Query head h reads K/V
+head h // (H // H_kv): multi-query (H_kv = 1) and grouped-query attention as
+compared in the llm-kernel-lib page's "Ablation Study"."""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as gen
+import oracle
+from parity import compare, gpu_forward, sample_rows
+from test_gpu_decode import ref_decode, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,dtype,causal,lens", [
+    (2, 8, 2, 300, 300, 64, "bf16", True, None),        # 4 query heads per K/V head
+    (2, 6, 3, 257, 257, 64, "f16", False, (0, 257)),    # pairs, padding incl. kv_len 0
+    (1, 4, 1, 200, 333, 128, "f16", True, (100, 333)),  # multi-query, Nq < Nk, d = 128
+    (1, 16, 2, 129, 65, 128, "bf16", False, None),      # 8 per K/V head, ragged tails
+])
+def test_gqa_forward_parity(B, H, Hkv, Nq, Nk, d, dtype, causal, lens):
+    w = gen.fwd_inputs(B, H, Nq, Nk, d, dtype, seed=7000 + B * 100 + H * 10 + Hkv,
+                       causal=causal, scale=1.0 / math.sqrt(d), kv_len_range=lens, Hkv=Hkv)
+    o, lse = gpu_forward(w)
+    o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, w.kv_lens)
+    what = f"gqa fwd B{B} H{H}/{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} lens={lens}"
+    print(what, compare(o, lse, o_ref, lse_ref, what), flush=True)
+
+
+def test_gqa_forward_equals_mha_on_repeated_heads_bitwise():
+    """Only the K/V addressing changes: the result must be the multi-head one on
+    K/V repeated per query head, bit for bit."""
+    w = gen.fwd_inputs(2, 8, 200, 200, 64, "bf16", seed=7100, causal=True, Hkv=2)
+    rep = gen.FwdInputs(w.q, np.repeat(w.k, 4, axis=1), np.repeat(w.v, 4, axis=1), w.dtype,
+                        w.scale, w.causal, w.kv_lens, w.seed)
+    o1, l1 = gpu_forward(w)
+    o2, l2 = gpu_forward(rep)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_gqa_entry_with_as_many_kv_heads_is_fa_fwd_bitwise():
+    import torch
+
+    import flashattention_forward_03_amd as fa
+    from parity import device_tensors
+
+    w = gen.fwd_inputs(3, 8, 130, 130, 64, "bf16", seed=7200, causal=True,
+                       kv_len_range=(60, 130))
+    q, k, v, kl = device_tensors(w)
+    o1, l1 = fa.forward(q, k, v, scale=w.scale, causal=True, kv_lens=kl)   # fa_fwd
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    st = fa.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(),
+                       3, 8, 8, 130, 130, 64, w.scale, 1, kl.data_ptr(), fa.FA_DTYPE_BF16,
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_forward_full_size_sampled():
+    """The causal B8 H16 N4096 d64 launch with 4 K/V heads; sampled rows."""
+    name = "fwd_causal_b8h16kv4_n4096_d64_bf16"
+    w = gen.fwd_workload(name)
+    B, H, Nq, Nk, d = w.shape
+    o, lse = gpu_forward(w)
+    rows = sample_rows(B, H, Nq, 2000, seed=w.seed,
+                       full_heads=((0, 0), (0, 3), (B - 1, H - 1)))
+    o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, None,
+                                          rows=rows)
+    stats = compare(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, name)
+    print(name, len(rows), "rows", stats, flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("S,H,Hkv,d,lens,dtype", [
+    (4, 8, 4, 128, (1, 600), "bf16"),     # 2 query heads per K/V head
+    (4, 8, 2, 128, (300, 700), "f16"),    # 4 per K/V head
+    (3, 16, 2, 64, (1, 1500), "bf16"),    # 8 per K/V head, d = 64
+    (3, 6, 2, 128, (20, 530), "bf16"),    # 3 per K/V head (padded slice)
+    (2, 12, 2, 64, (200, 300), "f16"),    # 6 per K/V head (padded slice)
+    (3, 16, 1, 128, (1, 900), "bf16"),    # multi-query: two slices of 8 heads
+    (2, 32, 1, 64, (500, 520), "f16"),    # multi-query: four slices of 8 heads
+])
+def test_gqa_decode_parity(S, H, Hkv, d, lens, dtype):
+    inp = gen.decode_inputs(S, H, d, lens, dtype, seed=8000 + S * 100 + H + Hkv + d,
+                            page_size=16, num_pages=512, Hkv=Hkv)
+    o, lse = run_decode(inp)
+    o_ref, lse_ref = ref_decode(inp)
+    what = f"gqa decode S{S} H{H}/{Hkv} d{d} lens{lens} {dtype}"
+    print(what, compare(o, lse, o_ref, lse_ref, what), flush=True)
+
+
+def test_gqa_decode_entry_with_as_many_kv_heads_is_fa_decode_paged_bitwise():
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    inp = gen.decode_inputs(5, 5, 64, (1, 600), "bf16", seed=8200, page_size=16, num_pages=256)
+    kp = gen.build_pool_device(inp, "k", "cuda")
+    vp = gen.build_pool_device(inp, "v", "cuda")
+    q = gen.to_torch(inp.q, "bf16").cuda()
+    pt = torch.from_numpy(inp.page_table).cuda()
+    kl = torch.from_numpy(inp.kv_lens).cuda()
+    o1, l1 = fa.decode_paged(q, kp, vp, pt, kl, scale=inp.scale)   # fa_decode_paged
+    mp = inp.page_table.shape[1]
+    ws = torch.empty(max(16, fa.fa_decode_workspace_bytes(5, 5, 64, mp, 16)), dtype=torch.uint8,
+                     device="cuda")
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    st = fa.fa_decode_paged_gqa(q.data_ptr(), kp.data_ptr(), vp.data_ptr(), pt.data_ptr(),
+                                kl.data_ptr(), o2.data_ptr(), l2.data_ptr(), 5, 5, 5, 64, 16, mp,
+                                inp.num_pages, inp.scale, fa.FA_DTYPE_BF16, ws.data_ptr(),
+                                ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_decode_zero_length_sequence():
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    inp = gen.decode_inputs(3, 8, 128, (5, 900), "bf16", seed=8100, page_size=16,
+                            num_pages=256, Hkv=2)
+    kp = gen.build_pool_device(inp, "k", "cuda")
+    vp = gen.build_pool_device(inp, "v", "cuda")
+    lens = inp.kv_lens.copy()
+    lens[1] = 0
+    q = gen.to_torch(inp.q, "bf16").cuda()
+    o, lse = fa.decode_paged(q, kp, vp, torch.from_numpy(inp.page_table).cuda(),
+                             torch.from_numpy(lens).cuda(), scale=inp.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    o_ref, lse_ref = ref_decode(inp)
+    for s in (0, 2):
+        compare(o[s], lse[s], o_ref[s], lse_ref[s], f"seq {s}")
+
+
+def test_gqa_decode_full_batch():
+    """32 sequences x 32 query heads over 8 K/V heads, d=128, lengths 512..8192,
+    pages scattered over a 65536-page pool."""
+    inp = gen.decode_workload("decode_paged_s32h32kv8_d128_bf16")
+    o, lse = run_decode(inp)
+    o_ref, lse_ref = ref_decode(inp)
+    print("gqa decode full", compare(o, lse, o_ref, lse_ref, "gqa decode full"), flush=True)
