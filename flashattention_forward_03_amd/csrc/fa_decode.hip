@@ -8,24 +8,33 @@
 // scores, online softmax (running max and normaliser, NanoInfer page "Online
 // Softmax"), rescaled accumulation of p * V.
 //
-// The work is bandwidth bound (one FMA per byte of K/V), so there is no MFMA
-// here: the kernel is laid out for HBM streaming.
-//   * Split-KV: one workgroup per (sequence, group of 4 heads, chunk of 16
-//     pages = 256 tokens) so that enough workgroups fill the 256 CUs even
-//     when a batch mixes short and long sequences.  Chunk boundaries depend
+// With one K/V head per query head the work is bandwidth bound (one FMA per
+// byte of K/V), so there is no MFMA here: the kernel is laid out for HBM
+// streaming.
+//   * Split-KV: work items of (sequence, chunk of 8 pages = 128 tokens,
+//     K/V head, slice of up to 8 of the query heads that share it
+//     (grouped-query attention, llm-kernel-lib page, "Ablation Study"));
+//     enough of them fill the 256 CUs even when a batch mixes short and
+//     long sequences (measured on MI355X: 8-page chunks beat 16 and 4 for
+//     both multi-head and grouped-query batches).  Chunk boundaries depend
 //     only on logical token positions.
-//   * One wave per head of the group.  The pool is [page, head, 16, d], so
-//     the group's rows of one page are 4 * 16 * d * 2 bytes contiguous (16 KB
-//     at d = 128): the four waves stream the same pages, and HBM sees
-//     contiguous 16 KB reads instead of scattered 4 KB ones (measured on
-//     MI355X: random 4 KB blocks read at ~5.2 TB/s, 16 KB blocks at ~6.1).
+//   * One wave per item, four items of consecutive K/V heads per workgroup.
+//     The pool is [page, K/V head, 16, d], so the four waves' rows of one
+//     page are 4 * 16 * d * 2 bytes contiguous (16 KB at d = 128): HBM sees
+//     contiguous 16 KB reads instead of scattered 4 KB ones (measured:
+//     random 4 KB blocks read at ~5.2 TB/s, 16 KB blocks at ~6.1).  Splitting
+//     a chunk's pages over the waves instead (more waves, 4 KB blocks) was
+//     measured slower except for single-sequence grouped-query batches.
 //   * Within a wave, token row r = lane / (d/8) with 8 consecutive head dims
 //     per lane: each wave step is one fully coalesced 16-byte load per lane
-//     for K and one for V; sixteen steps are loaded before any is used.
-//   * q.k is reduced over the d/8 lanes of a row with DPP moves; every lane
-//     keeps its own online-softmax state for its token stream; the streams
-//     of a wave are merged through LDS at the end of the chunk with the
-//     log-sum-exp rule.
+//     for K and one for V; up to sixteen steps are loaded before any is used.
+//     Every loaded K/V row serves all query heads of the wave's slice, so a
+//     K/V row is read once per slice, not once per query head.
+//   * q.k uses packed dot2 instructions on the raw f16/bf16 pairs, reduced
+//     over the d/8 lanes of a row with DPP moves; every lane keeps its own
+//     online-softmax state per query head for its token stream; the streams
+//     of a wave are merged with cross-lane moves at the end of the chunk
+//     with the log-sum-exp rule.
 //   * Chunks of one (sequence, head) are merged by a second small kernel with
 //     the same rule; a sequence with a single chunk is finished directly.
 #include "fa_common.h"

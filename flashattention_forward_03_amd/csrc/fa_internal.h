@@ -31,7 +31,7 @@ long long fwd_grid_size(int B, int H, int Nq);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
 // Decode: cached tokens per split-KV chunk, and the launch.
-constexpr int kDecodeChunkPages = 16;
+constexpr int kDecodeChunkPages = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

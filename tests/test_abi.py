@@ -125,9 +125,10 @@ def call_dec(**over):
 
 
 def test_decode_workspace_size(lib):
-    # 100 pages -> 7 chunks of 16 pages; per (s,h,chunk): d floats + (max, sum)
-    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 16) == 2 * 2 * 7 * (128 + 2) * 4
-    assert fa.fa_decode_workspace_bytes(2, 2, 128, 16, 16) == 0      # one chunk: none needed
+    # 100 pages -> 13 chunks of 8 pages; per (s,h,chunk): d floats + (max, sum)
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 16) == 2 * 2 * 13 * (128 + 2) * 4
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 8, 16) == 0       # one chunk: none needed
+    assert fa.fa_decode_workspace_bytes(2, 2, 128, 9, 16) == 2 * 2 * 2 * (128 + 2) * 4
     assert fa.fa_decode_workspace_bytes(2, 2, 96, 100, 16) == 0      # unsupported -> 0
     assert fa.fa_decode_workspace_bytes(2, 2, 128, 100, 8) == 0
 
@@ -145,7 +146,7 @@ def test_decode_workspace_size(lib):
     (dict(kp=A + 2), fa.FA_ERR_ALIGN),
     (dict(pt=A + 2), fa.FA_ERR_ALIGN),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
-    (dict(ws_bytes=2 * 2 * 4 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=2 * 2 * 13 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),   # one byte short
     (dict(ws=A + 4), fa.FA_ERR_ALIGN),
     (dict(S=0, q=None, o=None), fa.FA_OK),
 ])
@@ -192,8 +193,8 @@ def call_dec_gqa(H_kv, **over):
     (8, 2, dict(page_size=32), fa.FA_ERR_UNSUPPORTED),
     (8, 2, dict(kp=None), fa.FA_ERR_NULL),
     (8, 1, dict(ws=None), fa.FA_ERR_WORKSPACE),
-    # the workspace is sized by the QUERY heads: 8 heads x 7 chunks
-    (8, 2, dict(ws_bytes=2 * 8 * 7 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    # the workspace is sized by the QUERY heads: 8 heads x 13 chunks
+    (8, 2, dict(ws_bytes=2 * 8 * 13 * 130 * 4 - 1), fa.FA_ERR_WORKSPACE),
 ])
 def test_decode_gqa_argument_checks(lib, H, H_kv, over, status):
     assert call_dec_gqa(H_kv, H=H, **over) == status

@@ -65,8 +65,9 @@ def test_paged_equals_identity_table_bitwise(big):
 
 @pytest.mark.parametrize("S,H,d,lens,dtype,num_pages", [
     (5, 3, 128, (1, 40), "bf16", 64),            # < 1 page, ragged last page
-    (4, 2, 128, (500, 530), "f16", 256),          # around two chunks (256 tokens each)
-    (4, 2, 128, (250, 260), "bf16", 256),         # around one chunk
+    (4, 2, 128, (500, 530), "f16", 256),          # around four chunks (128 tokens each)
+    (4, 2, 128, (250, 260), "bf16", 256),         # around two chunks
+    (6, 2, 128, (120, 136), "bf16", 128),         # around one chunk
     (3, 2, 64, (1, 1500), "bf16", 512),           # d = 64, several chunks
     (2, 4, 64, (2000, 2100), "f16", 512),
     (7, 1, 128, (16, 16), "bf16", 16),            # exactly one page each
