@@ -6,15 +6,18 @@ device memory and the current stream.  There is no CPU path: if the library
 is missing or no GPU is present, calls raise.
 
 Two layers:
-  * ``fa_fwd``, ``fa_fwd_gqa``, ``fa_decode_paged``, ``fa_decode_paged_gqa``,
-    ``fa_decode_workspace_bytes``, ``fa_status_str``, ``fa_last_hip_error``:
-    the C entry points with the same names and arguments (raw device
-    addresses as ints, stream as int).
+  * ``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_ex``, ``fa_decode_paged``,
+    ``fa_decode_paged_gqa``, ``fa_decode_workspace_bytes``, ``fa_status_str``,
+    ``fa_last_hip_error``: the C entry points with the same names and
+    arguments (raw device addresses as ints, stream as int, strides as
+    3-tuples or None).
   * ``forward`` / ``decode_paged``: take torch tensors, check them, allocate
     the outputs (and the decode workspace), call the entry point on the
     current stream and raise ``FAError`` on a non-zero status.  The number
     of K/V heads is read from k (or the pools); fewer K/V heads than query
-    heads go to the ``_gqa`` entry point.
+    heads go to the ``_gqa`` entry point; non-contiguous tensors (any strides
+    with the head dim contiguous, e.g. a [B, N, H, d] buffer viewed as
+    [B, H, N, d]) or a 16-bit O go to ``fa_fwd_ex``.
 """
 from __future__ import annotations
 
@@ -36,8 +39,9 @@ FA_ERR_HIP = 6
 FA_ERR_ARG = 7
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F32 = 2
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_decode_paged", "fa_decode_paged_gqa",
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_decode_paged", "fa_decode_paged_gqa",
             "fa_decode_workspace_bytes", "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -86,6 +90,9 @@ def load_library():
     lib.fa_fwd.restype = I
     lib.fa_fwd_gqa.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     lib.fa_fwd_gqa.restype = I
+    S3 = ctypes.POINTER(ctypes.c_int64)
+    lib.fa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, F, I, P, I, I, P]
+    lib.fa_fwd_ex.restype = I
     lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode_paged.restype = I
     lib.fa_decode_paged_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
@@ -113,6 +120,21 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, kv_lens, d
                stream) -> int:
     return load_library().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal,
                                      kv_lens, dtype, stream)
+
+
+def _strides3(st):
+    if st is None:
+        return None
+    arr = (ctypes.c_int64 * 3)(*[int(x) for x in st])
+    return arr
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides,
+              scale, causal, kv_lens, dtype, o_dtype, stream) -> int:
+    return load_library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, _strides3(q_strides),
+                                    _strides3(k_strides), _strides3(v_strides),
+                                    _strides3(o_strides), scale, causal, kv_lens, dtype, o_dtype,
+                                    stream)
 
 
 def fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
@@ -161,11 +183,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
 
 
-def _check_dev(name, t):
+def _check_dev(name, t, contiguous=True):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.dim() > 0 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
 
 
 def _stream_handle(stream) -> int:
@@ -175,11 +199,14 @@ def _stream_handle(stream) -> int:
 
 
 def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
-            kv_lens=None, stream=None, out=None):
+            kv_lens=None, stream=None, out=None, out_dtype=None):
     """Exact attention forward: q [B, H, Nq, d], k/v [B, H_kv, Nk, d] f16/bf16
     (H a multiple of H_kv; query head h reads K/V head h // (H // H_kv)).
+    The tensors may be strided views (head dim contiguous).
 
-    Returns ``(o, lse)``: o float32 [B, H, Nq, d], lse float32 [B, H, Nq].
+    Returns ``(o, lse)``: o [B, H, Nq, d] in ``out_dtype`` (float32 by
+    default, or float16 / bfloat16), lse float32 [B, H, Nq].  ``out``: an
+    (o, lse) pair to write into; o may be a strided view, lse contiguous.
     ``kv_lens``: optional int32 GPU tensor [B] of valid key counts.
     """
     torch = _torch()
@@ -192,7 +219,7 @@ def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
     if Hkv < 1 or H % Hkv:
         raise ValueError("the query heads must be a multiple of the K/V heads")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t)
+        _check_dev(name, t, contiguous=False)
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -205,19 +232,40 @@ def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
             raise ValueError("kv_lens must be int32 [B]")
         kl_ptr = kv_lens.data_ptr()
     if out is None:
-        o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        odt = torch.float32 if out_dtype is None else out_dtype
+        o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    if Hkv == H:
+        if out_dtype is not None and o.dtype != out_dtype:
+            raise TypeError("out[0] does not have out_dtype")
+    if tuple(o.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out must be (o [B, H, Nq, d], lse [B, H, Nq])")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32")
+    _check_dev("o", o, contiguous=False)
+    odc = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+           torch.bfloat16: FA_DTYPE_BF16}.get(o.dtype)
+    if odc is None:
+        raise TypeError(f"o must be float32, float16 or bfloat16, got {o.dtype}")
+    plain = (odc == FA_DTYPE_F32 and all(t.is_contiguous() for t in (q, k, v, o)))
+    if plain and Hkv == H:
         st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
                     Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt, _stream_handle(stream))
-    else:
+        name = "fa_fwd"
+    elif plain:
         st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B,
                         H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt,
                         _stream_handle(stream))
+        name = "fa_fwd_gqa"
+    else:
+        st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                       Hkv, Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3],
+                       o.stride()[:3], float(scale), int(bool(causal)), kl_ptr, dt, odc,
+                       _stream_handle(stream))
+        name = "fa_fwd_ex"
     if st != FA_OK:
-        raise FAError(st, "fa_fwd" if Hkv == H else "fa_fwd_gqa")
+        raise FAError(st, name)
     return o, lse
 
 

@@ -64,38 +64,71 @@ const char *fa_status_str(int status)
 
 int fa_last_hip_error(void) { return g_last_hip_error; }
 
-int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv,
-               int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int H_kv, int Nq,
+              int Nk, int d, const int64_t *q_strides, const int64_t *k_strides, const int64_t *v_strides,
+              const int64_t *o_strides, float scale, int causal, const int32_t *kv_lens, int dtype, int o_dtype,
+              void *stream)
 {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
         return FA_ERR_SHAPE;
     if (H > 0 && (H_kv < 1 || H % H_kv != 0))
         return FA_ERR_SHAPE;
-    if (d != 64 && d != 128)
+    if (d < 8 || d > 128 || d % 8 != 0)
         return FA_ERR_UNSUPPORTED;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (o_dtype != FA_DTYPE_F16 && o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
         return FA_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1)
         return FA_ERR_ARG;
     if (!scale_ok(scale))
         return FA_ERR_ARG;
+    // strides: NULL = contiguous [B, heads, rows, d]
+    fa::FwdLayout lay{};
+    const int64_t *given[4] = {q_strides, k_strides, v_strides, o_strides};
+    long long *dst[4] = {lay.qs, lay.ks, lay.vs, lay.os};
+    const long long heads[4] = {H, H_kv, H_kv, H}, rows[4] = {Nq, Nk, Nk, Nq};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 3; ++j) {
+            const long long def = j == 0 ? heads[i] * rows[i] * d : (j == 1 ? rows[i] * d : d);
+            dst[i][j] = given[i] ? given[i][j] : def;
+            if (dst[i][j] < 0)
+                return FA_ERR_SHAPE;
+        }
+        if (dst[i][2] < d)   // rows must not overlap
+            return FA_ERR_SHAPE;
+    }
+    lay.d = d;
+    lay.o_kind = o_dtype == FA_DTYPE_F32 ? fa::FA_O_F32 : (o_dtype == FA_DTYPE_BF16 ? fa::FA_O_BF16 : fa::FA_O_F16);
     if (B == 0 || H == 0 || Nq == 0)
         return FA_OK;
     if (fa::fwd_grid_size(B, H, Nq) > INT_MAX)
         return FA_ERR_SHAPE;
-    if (((long long)Nk + 64) * d * 2 > INT_MAX)   // per-(b, h) key span: 32-bit buffer offsets
+    // the keys of one (b, K/V head) are addressed with 32-bit byte offsets
+    if (((long long)Nk + 64) * lay.ks[2] * 2 > INT_MAX || ((long long)Nk + 64) * lay.vs[2] * 2 > INT_MAX)
         return FA_ERR_SHAPE;
     if (!q || !o || !lse || (Nk > 0 && (!k || !v)))
         return FA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
         !aligned(kv_lens, 4))
         return FA_ERR_ALIGN;
+    // 16-byte Q / K / V row pieces; 4-element O stores (16 or 8 bytes)
+    for (int j = 0; j < 3; ++j)
+        if (lay.qs[j] % 8 || lay.ks[j] % 8 || lay.vs[j] % 8 || lay.os[j] % 4)
+            return FA_ERR_ALIGN;
 
-    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal == 1, dtype == FA_DTYPE_BF16, kv_lens};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, Nq, Nk, scale, causal == 1, dtype == FA_DTYPE_BF16, kv_lens, lay};
     const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "fa_fwd launch");
     return FA_OK;
+}
+
+int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv,
+               int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+{
+    return fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, nullptr, nullptr, nullptr, nullptr, scale, causal,
+                     kv_lens, dtype, FA_DTYPE_F32, stream);
 }
 
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int Nq,

@@ -73,6 +73,24 @@ __device__ __forceinline__ int swz_k(int row)
 }
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
 
+// LDS slot of 16-byte chunk c of a row with DC chunks under row key s (0..7):
+// an XOR inside aligned groups of 8 chunks (4 for a short row or the last
+// group of a 12-chunk row), so the slot stays inside the row; it is its own
+// inverse.
+template <int DC>
+__device__ __forceinline__ int swz_slot(int c, int s)
+{
+    if constexpr (DC == 4)
+        return c ^ (s & 3);
+    else if constexpr (DC % 8 == 0)
+        return c ^ s;
+    else
+        return c < 8 ? (c ^ s) : (8 | ((c & 3) ^ (s & 3)));
+}
+
+// LDS tile geometry for a padded head dim D in {32, 64, 96, 128}; the
+// actual head dim d <= D (a multiple of 8) fills the first d columns and
+// the rest read as zero.
 template <int D>
 struct Geometry {
     static constexpr int DC = D / 8;                 // 16-byte chunks per row
@@ -84,27 +102,34 @@ struct Geometry {
     static constexpr int TILE = BN * ROWB;           // bytes per K (or V) tile
     static constexpr int PIECES = TILE / 1024;       // 1 KB DMA pieces per tile
     static constexpr int PIECES_PER_WAVE = PIECES / 4;
-    static constexpr int ROWS_PER_PIECE = 1024 / ROWB;
     static_assert(PIECES_PER_WAVE * 4 == PIECES, "tile must split over 4 waves");
 };
 
 // Copy key rows [kt0, kt0 + BN) of one (b, h) into an LDS tile with the
 // buffer-to-LDS load (16 bytes per lane).  The buffer resource covers the
-// Nk rows of this (b, h); rows past Nk are out of range and read as zero
-// (those keys are always masked).  off[u] is the lane's byte offset for its
-// u-th 1 KB piece of tile 0 (chunk picked so that it lands in its swizzled
-// LDS slot).
+// Nk rows of this (b, h) (row stride rs bytes); rows past Nk are out of
+// range and read as zero (those keys are always masked).  off[u] is the
+// lane's byte offset for its u-th 1 KB piece of tile 0 (chunk picked so
+// that it lands in its swizzled LDS slot); step[u] is what one tile row
+// adds to it: 0 for the padding columns past d, whose offset lies beyond
+// any buffer range so that they read as zero.
+constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any buffer range (< 2^31 bytes)
+
 template <int D, bool IS_K>
-__device__ __forceinline__ void dma_offsets(int wave, int lane, unsigned (&off)[Geometry<D>::PIECES_PER_WAVE])
+__device__ __forceinline__ void dma_offsets(int wave, int lane, int d, unsigned rs,
+                                            unsigned (&off)[Geometry<D>::PIECES_PER_WAVE],
+                                            unsigned (&step)[Geometry<D>::PIECES_PER_WAVE])
 {
     using G = Geometry<D>;
 #pragma unroll
     for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
-        const int piece = u * 4 + wave;
-        const int row = piece * G::ROWS_PER_PIECE + lane / G::DC;
-        const int pc = lane % G::DC;
-        const int lc = pc ^ (IS_K ? swz_k(row) : swz_v(row));
-        off[u] = (unsigned)(row * D + lc * 8) * 2u;
+        const int slot = (u * 4 + wave) * 64 + lane;   // 16-byte slot of the tile
+        const int row = slot / G::DC;
+        const int pc = slot - row * G::DC;
+        const int lc = swz_slot<G::DC>(pc, IS_K ? swz_k(row) : swz_v(row));
+        const bool valid = lc * 8 < d;
+        off[u] = valid ? (unsigned)row * rs + (unsigned)lc * 16u : kOutOfRange;
+        step[u] = valid ? rs : 0u;
     }
 }
 
@@ -130,7 +155,7 @@ __device__ __forceinline__ u32x4s_t make_rsrc(const void *base, int nbytes)
 }
 
 template <int D>
-__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, int kt0,
+__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, const unsigned *step, int kt0,
                                          unsigned char *dst, int wave)
 {
     using G = Geometry<D>;
@@ -138,7 +163,7 @@ __device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *o
     for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
         const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
-        const uint32_t voff = off[u] + (unsigned)kt0 * G::ROWB;
+        const uint32_t voff = off[u] + (unsigned)kt0 * step[u];
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                      :
                      : "v"(voff), "s"(lds_addr), "s"(rsrc)
@@ -159,7 +184,7 @@ __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk
         const int sw = swz_k(row);
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c)
-            ka[blk][c] = *reinterpret_cast<const u32x4_t *>(rp + (((2 * c + hh) ^ sw) << 4));
+            ka[blk][c] = *reinterpret_cast<const u32x4_t *>(rp + (swz_slot<G::DC>(2 * c + hh, sw) << 4));
     }
 #pragma unroll
     for (int c = 0; c < G::KSTEPS; ++c)
@@ -186,8 +211,8 @@ __device__ __forceinline__ void pv_operands(const unsigned char *vb, int lane, i
         for (int c = 0; c < G::PCH; ++c) {
             const int r0 = 16 * c + 8 * hh + (j16 >> 2);
             const int r1 = r0 + 4;
-            const unsigned char *a0 = vb + r0 * G::ROWB + ((chunk ^ swz_v(r0)) << 4) + half;
-            const unsigned char *a1 = vb + r1 * G::ROWB + ((chunk ^ swz_v(r1)) << 4) + half;
+            const unsigned char *a0 = vb + r0 * G::ROWB + (swz_slot<G::DC>(chunk, swz_v(r0)) << 4) + half;
+            const unsigned char *a1 = vb + r1 * G::ROWB + (swz_slot<G::DC>(chunk, swz_v(r1)) << 4) + half;
             const u32x2_t y0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a0));
             const u32x2_t y1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a1));
             va[db][c] = u32x4_t{y0[0], y0[1], y1[0], y1[1]};
@@ -323,15 +348,30 @@ __device__ __forceinline__ void wait_vmcnt()
 
 template <int D>
 struct Pipe {
-    static constexpr int STAGES = D == 64 ? 3 : 2;             // LDS ring depth (tiles)
+    static constexpr int STAGES = D == 128 ? 2 : 3;            // LDS ring depth (tiles)
     static constexpr int DMA_PER_TILE = 2 * Geometry<D>::PIECES_PER_WAVE;   // per thread: K + V
 };
 
-// One query tile (BM rows of one (b, h)) against its key tiles.
+// Store 4 consecutive O values of one row in the output element type.
+__device__ __forceinline__ void store_o4(void *row, int dim0, int o_kind, float a, float b, float c, float e)
+{
+    if (o_kind == FA_O_F32) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(row) + dim0) = f32x4_t{a, b, c, e};
+    } else {
+        const u32x2_t v = o_kind == FA_O_BF16 ? u32x2_t{pack2<true>(a, b), pack2<true>(c, e)}
+                                              : u32x2_t{pack2<false>(a, b), pack2<false>(c, e)};
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(row) + dim0) = v;
+    }
+}
+
+// One query tile (BM rows of one (b, h)) against its key tiles.  Qb, Kb, Vb,
+// Ob, LSEb point at row 0 of this (b, h); qsn / osn are row strides in
+// elements, krs / vrs in bytes.
 template <int D, bool BF16>
 __device__ __forceinline__ void attend_qtile(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kb, const uint16_t *__restrict__ Vb,
-    float *__restrict__ O, float *__restrict__ LSE, size_t bh, int Nq, int Nk, int kvlen, int q0,
+    const uint16_t *__restrict__ Qb, long long qsn, const uint16_t *__restrict__ Kb, unsigned krs,
+    const uint16_t *__restrict__ Vb, unsigned vrs, void *__restrict__ Ob, long long osn, int o_kind,
+    float *__restrict__ LSEb, int d, int Nq, int Nk, int kvlen, int q0,
     float c_log2, float scale, bool causal, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
     unsigned char *const (&vbuf)[Pipe<D>::STAGES], int wave, int lane)
 {
@@ -365,27 +405,28 @@ __device__ __forceinline__ void attend_qtile(
     RowState st{-INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
-    const u32x4s_t krs = make_rsrc(Kb, Nk * G::ROWB), vrs = make_rsrc(Vb, Nk * G::ROWB);
+    const u32x4s_t krsrc = make_rsrc(Kb, Nk * krs), vrsrc = make_rsrc(Vb, Nk * vrs);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, koff);
-    dma_offsets<D, false>(wave, lane, voff);
+    unsigned kstep[G::PIECES_PER_WAVE], vstep[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, d, krs, koff, kstep);
+    dma_offsets<D, false>(wave, lane, d, vrs, voff, vstep);
 
     // prologue: the first ST-1 tiles in flight
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
         if (i < n_tiles) {
-            dma_tile<D>(krs, koff, i * BN, kbuf[i], wave);
-            dma_tile<D>(vrs, voff, i * BN, vbuf[i], wave);
+            dma_tile<D>(krsrc, koff, kstep, i * BN, kbuf[i], wave);
+            dma_tile<D>(vrsrc, voff, vstep, i * BN, vbuf[i], wave);
         }
 
     // Q after the prologue copies; the empty asm makes the compiler wait for
     // it here, once, instead of at the loop head on every iteration
     u32x4_t qf[G::KSTEPS];
     {
-        const uint16_t *qp = Q + (bh * Nq + (qrow < Nq ? qrow : 0)) * D + 8 * hh;
+        const uint16_t *qp = Qb + (qrow < Nq ? qrow : 0) * qsn + 8 * hh;
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c)
-            qf[c] = qrow < Nq ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
+            qf[c] = (qrow < Nq && 16 * c + 8 * hh < d) ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c)
             asm volatile("" : "+v"(qf[c]));
@@ -402,8 +443,8 @@ __device__ __forceinline__ void attend_qtile(
             wait_vmcnt<0>();
         __syncthreads();
         if (t + ST - 1 < n_tiles) {
-            dma_tile<D>(krs, koff, (t + ST - 1) * BN, kfill, wave);
-            dma_tile<D>(vrs, voff, (t + ST - 1) * BN, vfill, wave);
+            dma_tile<D>(krsrc, koff, kstep, (t + ST - 1) * BN, kfill, wave);
+            dma_tile<D>(vrsrc, voff, vstep, (t + ST - 1) * BN, vfill, wave);
         }
         if (t < wave_tiles) {
             const int kt0 = t * BN;
@@ -444,21 +485,24 @@ __device__ __forceinline__ void attend_qtile(
     }
     __syncthreads();   // the ring is reused by the next query tile of this workgroup
 
-    // ---- epilogue: O = O_acc / l, LSE = m * scale + ln(l)
+    // ---- epilogue: O = O_acc / l (columns < d, in the output type),
+    // LSE = m * scale + ln(l)
     const float l_tot = st.l + other_half(st.l);
     if (qrow < Nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *op = O + (bh * Nq + qrow) * D + 4 * hh;
+        void *orow = o_kind == FA_O_F32 ? (void *)(static_cast<float *>(Ob) + qrow * osn)
+                                        : (void *)(static_cast<uint16_t *>(Ob) + qrow * osn);
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4_t v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                             oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-                *reinterpret_cast<f32x4_t *>(op + 32 * db + 8 * g) = v;
+                const int dim0 = 32 * db + 8 * g + 4 * hh;
+                if (dim0 < d)
+                    store_o4(orow, dim0, o_kind, oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                             oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
             }
         if (hh == 0)
-            LSE[bh * Nq + qrow] = l_tot > 0.f ? st.m * scale + __log2f(l_tot) * kLn2 : -INFINITY;
+            LSEb[qrow] = l_tot > 0.f ? st.m * scale + __log2f(l_tot) * kLn2 : -INFINITY;
     }
 }
 
@@ -473,10 +517,10 @@ __device__ __forceinline__ void attend_qtile(
 // receives a contiguous range.
 // The causal flag is a runtime argument: both modes share one code path.
 template <int D, bool BF16>
-__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
+__global__ __launch_bounds__(NTHREADS, D <= 64 ? 3 : 2) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ LSE, int H, int Hkv, int Nq, int Nk, int n_qtiles, int n_units,
-    float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
+    void *__restrict__ O, float *__restrict__ LSE, FwdLayout lay, int H, int Hkv, int Nq, int Nk, int n_qtiles,
+    int n_units, float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
     constexpr int ST = Pipe<D>::STAGES;
@@ -507,19 +551,23 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void fwd_kernel(
         bhi = logical / n_units;
         qt = logical - bhi * n_units;
     }
-    const size_t bh = (size_t)bhi;
     const int b = bhi / H;
-    const size_t kvh = (size_t)b * Hkv + (bhi - b * H) / (H / Hkv);   // K/V head of this query head
+    const int h = bhi - b * H;
+    const int kvh = h / (H / Hkv);   // K/V head of this query head
     int kvlen = Nk;
     if (kv_lens) {
         kvlen = kv_lens[b];
         kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
     }
-    const uint16_t *Kb = K + kvh * Nk * D;
-    const uint16_t *Vb = V + kvh * Nk * D;
+    const uint16_t *Qb = Q + b * lay.qs[0] + h * lay.qs[1];
+    const uint16_t *Kb = K + b * lay.ks[0] + kvh * lay.ks[1];
+    const uint16_t *Vb = V + b * lay.vs[0] + kvh * lay.vs[1];
+    const long long oe = b * lay.os[0] + h * lay.os[1];
+    void *Ob = lay.o_kind == FA_O_F32 ? (void *)(static_cast<float *>(O) + oe) : (void *)(static_cast<uint16_t *>(O) + oe);
 
-    attend_qtile<D, BF16>(Q, Kb, Vb, O, LSE, bh, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal, kbuf, vbuf,
-                          wave, lane);
+    attend_qtile<D, BF16>(Qb, lay.qs[2], Kb, (unsigned)(lay.ks[2] * 2), Vb, (unsigned)(lay.vs[2] * 2), Ob, lay.os[2],
+                          lay.o_kind, LSE + (size_t)bhi * Nq, lay.d, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal,
+                          kbuf, vbuf, wave, lane);
 }
 
 int units_per_head(int Nq, bool causal)
@@ -536,7 +584,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     const int n_units = units_per_head(a.Nq, a.causal);
     const long long grid = (long long)n_units * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse, a.lay,
                        a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.causal ? 1 : 0,
                        a.kv_lens);
     return hipGetLastError();
@@ -548,8 +596,14 @@ long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1)
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {
-    if (a.d == 64)
+    // LDS geometry of the smallest padded head dim that holds d
+    const int d = a.lay.d;
+    if (d <= 32)
+        return a.bf16 ? launch<32, true>(a, stream) : launch<32, false>(a, stream);
+    if (d <= 64)
         return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    if (d <= 96)
+        return a.bf16 ? launch<96, true>(a, stream) : launch<96, false>(a, stream);
     return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }
 

@@ -7,13 +7,29 @@
 
 namespace fa {
 
+// Output element types of the forward's O.
+constexpr int FA_O_F16 = 0;
+constexpr int FA_O_BF16 = 1;
+constexpr int FA_O_F32 = 2;
+
+// Forward layout, passed to the kernel by value: element strides (batch,
+// head, row) of Q, K, V and O (head dim contiguous), the head dim d and
+// O's element type.
+struct FwdLayout {
+    long long qs[3], ks[3], vs[3], os[3];
+    int d;
+    int o_kind;
+};
+
 struct FwdArgs {
     const void *q, *k, *v;
-    float *o, *lse;
-    int B, H, Hkv, Nq, Nk, d;   // query head h reads K/V head h / (H / Hkv)
+    void *o;
+    float *lse;
+    int B, H, Hkv, Nq, Nk;   // query head h reads K/V head h / (H / Hkv)
     float scale;
     bool causal, bf16;
     const int32_t *kv_lens;
+    FwdLayout lay;
 };
 
 struct DecodeArgs {

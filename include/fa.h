@@ -1,7 +1,9 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library.
  *
- * Two operations, both asynchronous on the caller's HIP stream:
+ * Two operations, both asynchronous on the caller's HIP stream (each also with
+ * grouped-query heads, the _gqa calls; the forward also with strides and a
+ * 16-bit O, fa_fwd_ex):
  *
  *   fa_fwd           exact attention forward: O = softmax(scale * Q K^T + mask) V
  *                    and the per-row log-sum-exp, computed tile by tile with an
@@ -63,9 +65,10 @@ extern "C" {
 #define FA_ERR_HIP 6         /* a HIP launch failed; see fa_last_hip_error() */
 #define FA_ERR_ARG 7         /* scale not finite and > 0, or causal not 0/1 */
 
-/* element types of Q, K, V (and the KV pools) */
+/* element types of Q, K, V (and the KV pools); FA_DTYPE_F32 only for fa_fwd_ex's O */
 #define FA_DTYPE_F16 0
 #define FA_DTYPE_BF16 1
+#define FA_DTYPE_F32 2
 
 /*
  * Exact attention forward.
@@ -76,7 +79,8 @@ extern "C" {
  *   lse      [B, H, Nq]     float32 output (written): natural log of the sum of
  *                           exp(scaled scores) over the row's valid keys;
  *                           4-byte aligned
- *   d        64 or 128
+ *   d        a multiple of 8 from 8 to 128 (the Kernel-Inference-Engine page's
+ *            head-dim templates 32, 64, 80, 96, 128 among them)
  *   scale    multiplies Q.K (finite, > 0; typically 1/sqrt(d))
  *   causal   0 or 1.  Query row i may see key j only if j <= i + (Nk - Nq)
  *            (aligned at the bottom-right; plain lower-triangular when Nq == Nk)
@@ -108,6 +112,35 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
 int fa_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
                int H_kv, int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens,
                int dtype, void *stream);
+
+/*
+ * fa_fwd_gqa with explicit strides and a choice of O's element type, for
+ * tensors that live inside larger buffers (e.g. [B, N, H, d] "BSHD"
+ * activations, or a fused QKV projection output):
+ *
+ *   q_strides, k_strides, v_strides, o_strides
+ *            int64[3] in ELEMENTS: the distance between consecutive batches,
+ *            heads and rows (query/key positions) of that tensor; the head dim
+ *            is always contiguous.  NULL = the contiguous [B, heads, N, d]
+ *            layout of fa_fwd.  Each value must be >= 0, the row stride >= d;
+ *            q/k/v strides a multiple of 8, o strides a multiple of 4 (else
+ *            FA_ERR_ALIGN).  Zero batch/head strides may broadcast q/k/v; O
+ *            rows of different (b, h, row) must not overlap (else the result is
+ *            unspecified).
+ *   o        written in o_dtype: FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16
+ *            (O is formed in fp32, divided by the row sum, then rounded to
+ *            nearest even).
+ *   lse      always fp32, contiguous [B, H, Nq].
+ *
+ * The keys of one (b, K/V head) are addressed with 32-bit byte offsets:
+ * (Nk + 64) * row_stride * 2 must stay below 2^31 for K and V (else
+ * FA_ERR_SHAPE).  Everything else as for fa_fwd_gqa.
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int H_kv, int Nq, int Nk, int d, const int64_t *q_strides,
+              const int64_t *k_strides, const int64_t *v_strides, const int64_t *o_strides,
+              float scale, int causal, const int32_t *kv_lens, int dtype, int o_dtype,
+              void *stream);
 
 /*
  * Decode attention over a paged KV cache (query length 1).

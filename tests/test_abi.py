@@ -57,7 +57,8 @@ def call_fwd(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(B=-1), fa.FA_ERR_SHAPE),
     (dict(Nk=-3), fa.FA_ERR_SHAPE),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),    # head dims: multiples of 8 from 8 to 128
+    (dict(d=136), fa.FA_ERR_UNSUPPORTED),
     (dict(d=0), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
     (dict(causal=2), fa.FA_ERR_ARG),
@@ -102,7 +103,7 @@ def call_fwd_gqa(H_kv, **over):
     (4, 8, {}, fa.FA_ERR_SHAPE),        # more K/V heads than query heads
     (6, 4, {}, fa.FA_ERR_SHAPE),
     (0, 0, dict(q=None, o=None, lse=None), fa.FA_OK),   # no query head: empty problem
-    (4, 2, dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (4, 2, dict(d=92), fa.FA_ERR_UNSUPPORTED),
     (4, 2, dict(k=None), fa.FA_ERR_NULL),
     (4, 1, dict(v=A + 2), fa.FA_ERR_ALIGN),
     (4, 2, dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
@@ -207,3 +208,36 @@ def test_binding_checks_head_grouping(lib):
     k = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="multiple of the K/V heads"):
         fa.forward(q, k, k)
+
+
+def call_fwd_ex(qs=None, ks=None, vs=None, os_=None, o_dtype=fa.FA_DTYPE_F32, H_kv=1, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], H_kv, a["Nq"],
+                        a["Nk"], a["d"], qs, ks, vs, os_, a["scale"], a["causal"], a["kv_lens"],
+                        a["dtype"], o_dtype, a["stream"])
+
+
+# B=1, H=1, Nq=Nk=8, d=64 unless overridden; strides in elements (batch, head, row)
+@pytest.mark.parametrize("kw,status", [
+    (dict(o_dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(qs=(512, 512, -64)), fa.FA_ERR_SHAPE),          # negative stride
+    (dict(ks=(512, 512, 32)), fa.FA_ERR_SHAPE),           # rows overlap (row stride < d)
+    (dict(os_=(512, 512, 60)), fa.FA_ERR_SHAPE),
+    (dict(qs=(512, 512, 68)), fa.FA_ERR_ALIGN),           # q/k/v strides: multiples of 8
+    (dict(vs=(516, 512, 64)), fa.FA_ERR_ALIGN),
+    (dict(os_=(512, 514, 64)), fa.FA_ERR_ALIGN),          # o strides: multiples of 4
+    (dict(d=80, ks=(640, 640, 84)), fa.FA_ERR_ALIGN),     # 84 elements = 168 bytes
+    # K rows addressed with 32-bit byte offsets: (Nk + 64) * row stride * 2 < 2^31
+    (dict(Nk=1 << 20, ks=(0, 0, 1024)), fa.FA_ERR_SHAPE),
+    (dict(Nk=1 << 20, vs=(0, 0, 1024)), fa.FA_ERR_SHAPE),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=A + 8), fa.FA_ERR_ALIGN),
+    (dict(H=4, H_kv=3), fa.FA_ERR_SHAPE),
+    # empty problems: nothing to launch
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None, o_dtype=fa.FA_DTYPE_BF16), fa.FA_OK),
+    (dict(Nq=0, qs=(0, 0, 64), o_dtype=fa.FA_DTYPE_F16), fa.FA_OK),
+])
+def test_fwd_ex_argument_checks(lib, kw, status):
+    assert call_fwd_ex(**kw) == status
