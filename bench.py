@@ -19,6 +19,9 @@ Prints ONE JSON line.  ``value`` is forward TFLOP/s (nominal FLOPs
 peak; and
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 forward workload on the host cores (and reports the sample's parity).
+``variants`` times generalised forward launches outside the step (head dims
+32 / 96 / 128, [B, N, H, d] inputs with a bf16 O, 4 K/V heads) on the same
+causal B8 H16 N4096 shape, each against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -203,6 +206,58 @@ def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
     }
 
 
+# Generalised forward launches on the headline shape (causal B8 H16 N4096):
+# name -> (d, K/V heads, inputs stored [B, N, H, d], O dtype)
+VARIANTS = {
+    "fwd_causal_b8h16_n4096_d128_bf16": (128, 16, False, "f32"),
+    "fwd_causal_b8h16_n4096_d96_bf16": (96, 16, False, "f32"),
+    "fwd_causal_b8h16_n4096_d32_bf16": (32, 16, False, "f32"),
+    "fwd_causal_b8h16_n4096_d64_bf16_bshd_obf16": (64, 16, True, "bf16"),
+    "fwd_causal_b8h16kv4_n4096_d64_bf16": (64, 4, False, "f32"),
+}
+
+
+def time_variants(fa, dev, steps, warmup):
+    """Per variant: average launch time over `steps` launches (HIP events on
+    the launch stream) after `warmup`, and TFLOP/s against the bf16 peak.
+    Inputs are N(0, 1) from a seeded device generator (timing only; the
+    parity tests cover these launch configurations)."""
+    import torch
+
+    B, H, N = 8, 16, 4096
+    out = {}
+    g = torch.Generator(device=dev)
+    for i, (name, (d, hkv, bshd, odt)) in enumerate(VARIANTS.items()):
+        g.manual_seed(7000 + i)
+
+        def draw(heads):
+            shape = (B, N, heads, d) if bshd else (B, heads, N, d)
+            x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            return x.transpose(1, 2) if bshd else x
+
+        q, k, v = draw(H), draw(hkv), draw(hkv)
+        otd = {"f32": torch.float32, "bf16": torch.bfloat16}[odt]
+        o = torch.empty((B, N, H, d) if bshd else (B, H, N, d), dtype=otd, device=dev)
+        o = o.transpose(1, 2) if bshd else o
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        for _ in range(warmup):
+            fa.forward(q, k, v, scale=scale, causal=True, out=(o, lse))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            fa.forward(q, k, v, scale=scale, causal=True, out=(o, lse))
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        tf = attention_flops(B, H, N, N, d, True) / (ms / 1e3) / 1e12
+        out[name] = {"kernel_ms_avg": ms, "TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                     "d": d, "H_kv": hkv, "layout": "bshd" if bshd else "bhsd", "o_dtype": odt}
+        del q, k, v, o, lse
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +267,8 @@ def main():
                     help="target wall time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="time the forward only")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the generalised forward launches timed after the steps")
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -376,6 +433,9 @@ def main():
                          "frac": g_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic(GQA_TRAFFIC_FILE, DEC_SOURCES)},
         }
+    if not args.no_variants:
+        print("[bench] forward variants", file=sys.stderr, flush=True)
+        result["variants"] = time_variants(fa, dev, args.steps, args.warmup)
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, o.cpu().numpy(), lse.cpu().numpy(),

@@ -64,9 +64,9 @@ def test_head_dims(d, causal):
     print(what, compare(o, lse, *_ref(w), what), flush=True)
 
 
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 96, 128])
 def test_head_dims_full_size_sampled(d):
-    """B8 H16 N4096 causal bf16 at d = 32 / 96 (the launch the variants bench times)."""
+    """B8 H16 N4096 causal bf16 at d = 32 / 96 / 128 (launches the bench times)."""
     w = gen.fwd_inputs(8, 16, 4096, 4096, d, "bf16", seed=9100 + d, causal=True,
                        scale=1.0 / math.sqrt(d))
     B, H, Nq, Nk, _ = w.shape
