@@ -12,16 +12,16 @@
 //
 // gfx950 mapping:
 //   * workgroup = 4 waves = BM = 128 query rows (32 per wave) of one (b, h);
-//     three workgroups per CU (one wave of each per SIMD); causal tiles are
-//     dispatched heaviest first;
-//   * key tiles of BN = 64 rows.  K and V tiles are copied HBM/L2 -> LDS by
-//     the buffer-to-LDS load (16 bytes per lane, no VGPR staging); each lane
-//     fetches the chunk that belongs at its XOR-swizzled LDS slot, and rows
-//     past Nk fall outside the buffer range and read as zero.  The LDS ring
-//     holds three K and three V tiles (two for d = 128), filled two tiles
-//     ahead of use;
+//     four workgroups per CU at d = 64 (one wave of each per SIMD), three at
+//     d = 128, two at d = 96; causal tiles are dispatched heaviest first;
+//   * key tiles of 32 rows at d = 64 / 128, 64 at d = 32 / 96.  K and V tiles
+//     are copied HBM/L2 -> LDS by the buffer-to-LDS load (16 bytes per lane,
+//     no VGPR staging); each lane fetches the chunk that belongs at its
+//     XOR-swizzled LDS slot, and rows past Nk (and columns past d) fall
+//     outside the buffer range and read as zero.  The LDS ring holds three K
+//     and three V tiles (two at d = 128), filled two tiles ahead of use;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA so
-//     that each lane owns ONE query row (lane % 32) and 32 of its 64 scores:
+//     that each lane owns ONE query row (lane % 32) and half of its tile scores:
 //     the row sum is lane-local plus one permlane32 swap, and the
 //     accumulator registers are directly the B operand of the second MFMA;
 //   * O^T = V^T P^T with the same MFMA; V^T fragments come straight from the
@@ -45,7 +45,12 @@ namespace fa {
 namespace {
 
 constexpr int BM = 128;
-constexpr int BN = 64;
+// Key-tile rows per padded head dim: 32 where a 32-row tile still splits
+// into 1 KB copy pieces over the 4 waves (d = 64, 128); the smaller tile
+// frees the registers for one more wave per SIMD (measured faster: 4 waves
+// at d = 64, 3 at d = 128); 64 for d = 32, 96.
+template <int D>
+constexpr int kBN = (D == 64 || D == 128) ? 32 : 64;
 constexpr int NTHREADS = 256;
 // Bound on the probabilities formed against a stale running max, in
 // exponent (log2) units: f16 P must stay below 65504, bf16 has fp32's range.
@@ -95,6 +100,7 @@ template <int D>
 struct Geometry {
     static constexpr int DC = D / 8;                 // 16-byte chunks per row
     static constexpr int KSTEPS = D / 16;            // MFMA k-steps over d
+    static constexpr int BN = kBN<D>;                // key rows per tile
     static constexpr int NBLK = BN / 32;             // 32-key blocks per tile
     static constexpr int PCH = BN / 16;              // 16-key PV k-steps per tile
     static constexpr int DB = D / 32;                // 32-wide column blocks of O
@@ -173,7 +179,7 @@ __device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *o
 
 template <int D, bool BF16>
 __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk, int hh,
-                                        const u32x4_t (&qf)[D / 16], f32x16_t (&s)[BN / 32])
+                                        const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
 {
     using G = Geometry<D>;
     u32x4_t ka[G::NBLK][G::KSTEPS];
@@ -197,7 +203,7 @@ __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk
 // k = 8 consecutive tile keys), read with the transposing LDS read.
 template <int D>
 __device__ __forceinline__ void pv_operands(const unsigned char *vb, int lane, int hh,
-                                            u32x4_t (&va)[D / 32][BN / 16])
+                                            u32x4_t (&va)[D / 32][kBN<D> / 16])
 {
     using G = Geometry<D>;
     const int j16 = lane & 15;
@@ -222,11 +228,11 @@ __device__ __forceinline__ void pv_operands(const unsigned char *vb, int lane, i
 
 // O^T += V^T P^T for one tile; the two column blocks' MFMA chains alternate.
 template <int D, bool BF16>
-__device__ __forceinline__ void pv_mfma(const u32x4_t (&va)[D / 32][BN / 16], const u32x4_t (&pf)[BN / 16],
+__device__ __forceinline__ void pv_mfma(const u32x4_t (&va)[D / 32][kBN<D> / 16], const u32x4_t (&pf)[kBN<D> / 16],
                                         f32x16_t (&oacc)[D / 32])
 {
 #pragma unroll
-    for (int c = 0; c < BN / 16; ++c)
+    for (int c = 0; c < kBN<D> / 16; ++c)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
             oacc[db] = mma32<BF16>(va[db][c], pf[c], oacc[db]);
@@ -234,9 +240,9 @@ __device__ __forceinline__ void pv_mfma(const u32x4_t (&va)[D / 32][BN / 16], co
 
 template <int D, bool BF16>
 __device__ __forceinline__ void pv_tile(const unsigned char *vb, int lane, int hh,
-                                        const u32x4_t (&pf)[BN / 16], f32x16_t (&oacc)[D / 32])
+                                        const u32x4_t (&pf)[kBN<D> / 16], f32x16_t (&oacc)[D / 32])
 {
-    u32x4_t va[D / 32][BN / 16];
+    u32x4_t va[D / 32][kBN<D> / 16];
     pv_operands<D>(vb, lane, hh, va);
     pv_mfma<D, BF16>(va, pf, oacc);
 }
@@ -250,10 +256,10 @@ struct RowState {
 // Causal / padding mask: rel = number of valid keys counted from this lane's
 // first tile key (kt0 + 8*hh).
 template <int D>
-__device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int rel)
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[kBN<D> / 32], int rel)
 {
 #pragma unroll
-    for (int blk = 0; blk < BN / 32; ++blk)
+    for (int blk = 0; blk < kBN<D> / 32; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int koff = blk * 32 + 16 * (r >> 3) + (r & 7);
@@ -264,13 +270,12 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[BN / 32], int rel)
 // Probabilities of one tile against the row's current (possibly stale) max
 // m: p = exp2(s*c - m*c), packed to 16 bits for the MFMA, summed in fp32
 // (4 independent partial sums).  Returns the row sum of this lane's 32 p.
-template <bool BF16>
-__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[BN / 32], float mc, float c_log2,
-                                          u32x4_t (&pf)[BN / 16])
+template <int NB, bool BF16>
+__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, float c_log2, u32x4_t (&pf)[2 * NB])
 {
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int blk = 0; blk < BN / 32; ++blk)
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -295,8 +300,8 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[BN / 32], float mc
 // alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
 // uniform) when O must be multiplied by alpha (done by the caller).
 template <int D, bool BF16>
-__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowState &st,
-                                             u32x4_t (&pf)[BN / 16], float c_log2, float tau_log2,
+__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
+                                             u32x4_t (&pf)[kBN<D> / 16], float c_log2, float tau_log2,
                                              float &alpha)
 {
     const float limit = exp2f(tau_log2);
@@ -305,7 +310,7 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
     bool rescale = false;
     // at most two passes: the second one runs against the exact max (p <= 1)
     for (int pass = 0; pass < 2; ++pass) {
-        const float psum = exp_tile<BF16>(s, mc, c_log2, pf);
+        const float psum = exp_tile<kBN<D> / 32, BF16>(s, mc, c_log2, pf);
         const bool bad = pass == 0 && (st.m == -INFINITY || !(psum <= limit));
         if (__builtin_amdgcn_ballot_w64(bad) == 0) {
             st.l = fmaf(st.l, alpha, psum);
@@ -314,7 +319,7 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[BN / 32], RowSt
         // exact path: tile max (lane-local, then the other half of the wave)
         float mx = s[0][0];
 #pragma unroll
-        for (int blk = 0; blk < BN / 32; ++blk)
+        for (int blk = 0; blk < kBN<D> / 32; ++blk)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[blk][r]);
@@ -390,6 +395,7 @@ __device__ __forceinline__ void attend_qtile(
         const int wlast = min(wave_first_row + 32, Nq) - 1;
         wave_key_end = min(wave_key_end, max(wlast + dq + 1, 0));
     }
+    constexpr int BN = G::BN;
     const int n_tiles = (key_end + BN - 1) / BN;
     const int wave_tiles = min(n_tiles, (wave_key_end + BN - 1) / BN);
 
@@ -517,7 +523,7 @@ __device__ __forceinline__ void attend_qtile(
 // receives a contiguous range.
 // The causal flag is a runtime argument: both modes share one code path.
 template <int D, bool BF16>
-__global__ __launch_bounds__(NTHREADS, D <= 64 ? 3 : 2) void fwd_kernel(
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     void *__restrict__ O, float *__restrict__ LSE, FwdLayout lay, int H, int Hkv, int Nq, int Nk, int n_qtiles,
     int n_units, float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
