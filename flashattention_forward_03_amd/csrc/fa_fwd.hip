@@ -160,16 +160,24 @@ __device__ __forceinline__ u32x4s_t make_rsrc(const void *base, int nbytes)
     return r;
 }
 
+// The per-tile step is either kept per lane (step[]) or derived from the
+// out-of-range sentinel (rs): the second costs two VALU per copy and saves
+// the step registers, which lets d = 32 run 4 waves per SIMD and d = 128
+// spill less (measured faster there, slower at d = 64).
 template <int D>
-__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, const unsigned *step, int kt0,
-                                         unsigned char *dst, int wave)
+__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, const unsigned *step, unsigned rs,
+                                         int kt0, unsigned char *dst, int wave)
 {
     using G = Geometry<D>;
 #pragma unroll
     for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
         const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
-        const uint32_t voff = off[u] + (unsigned)kt0 * step[u];
+        uint32_t voff;
+        if constexpr (D == 64)
+            voff = off[u] + (unsigned)kt0 * step[u];
+        else
+            voff = off[u] == kOutOfRange ? kOutOfRange : off[u] + (unsigned)kt0 * rs;
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                      :
                      : "v"(voff), "s"(lds_addr), "s"(rsrc)
@@ -421,8 +429,8 @@ __device__ __forceinline__ void attend_qtile(
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
         if (i < n_tiles) {
-            dma_tile<D>(krsrc, koff, kstep, i * BN, kbuf[i], wave);
-            dma_tile<D>(vrsrc, voff, vstep, i * BN, vbuf[i], wave);
+            dma_tile<D>(krsrc, koff, kstep, krs, i * BN, kbuf[i], wave);
+            dma_tile<D>(vrsrc, voff, vstep, vrs, i * BN, vbuf[i], wave);
         }
 
     // Q after the prologue copies; the empty asm makes the compiler wait for
@@ -449,8 +457,8 @@ __device__ __forceinline__ void attend_qtile(
             wait_vmcnt<0>();
         __syncthreads();
         if (t + ST - 1 < n_tiles) {
-            dma_tile<D>(krsrc, koff, kstep, (t + ST - 1) * BN, kfill, wave);
-            dma_tile<D>(vrsrc, voff, vstep, (t + ST - 1) * BN, vfill, wave);
+            dma_tile<D>(krsrc, koff, kstep, krs, (t + ST - 1) * BN, kfill, wave);
+            dma_tile<D>(vrsrc, voff, vstep, vrs, (t + ST - 1) * BN, vfill, wave);
         }
         if (t < wave_tiles) {
             const int kt0 = t * BN;
