@@ -35,6 +35,8 @@ def _load():
         lib.oracle_fwd.restype = I
         lib.oracle_decode.argtypes = [P, P, P, P, I, I, I, I, I, D, P, P, I]
         lib.oracle_decode.restype = I
+        lib.oracle_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, I, P, P, L, P, P, P, P, I]
+        lib.oracle_bwd.restype = I
         lib.oracle_widen.argtypes = [P, I, L, P]
         lib.oracle_widen.restype = None
         _lib = lib
@@ -120,6 +122,42 @@ def decode(q, k, v, seq_off, dtype: str, scale: float, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle_decode self-check failed ({rc})")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, dtype: str, scale: float, causal: bool,
+                  kv_lens: Optional[np.ndarray] = None, groups=None, nthreads: int = 0):
+    """Gradients (float64) of exact attention for the output gradient ``dout``.
+
+    q, dout: [B,H,Nq,d]; k, v: [B,Hkv,Nk,d] uint16 bits.  Returns
+    (dq [B,H,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d], delta [B,H,Nq]) where
+    delta is the row term D_i = dO_i . O_i.  ``groups``: optional flat ids
+    b*Hkv + kvh; then only those K/V heads (and the query heads reading them)
+    are computed and every other entry is NaN.
+    """
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    v = np.ascontiguousarray(v, np.uint16)
+    g = np.ascontiguousarray(dout, np.uint16)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    assert Hkv >= 1 and H % Hkv == 0
+    assert k.shape == (B, Hkv, Nk, d) and v.shape == k.shape and g.shape == q.shape
+    kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, np.int32)
+    fill = np.nan if groups is not None else 0.0
+    dq = np.full((B, H, Nq, d), fill)
+    dk = np.full((B, Hkv, Nk, d), fill)
+    dv = np.full((B, Hkv, Nk, d), fill)
+    delta = np.full((B, H, Nq), fill)
+    gr = None if groups is None else np.ascontiguousarray(np.sort(np.asarray(groups, np.int64)))
+    if gr is not None:
+        assert gr.size == 0 or (gr[0] >= 0 and gr[-1] < B * Hkv)
+    rc = _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _DT[dtype], B, H, Hkv, Nq, Nk,
+                            d, float(scale), int(bool(causal)), _ptr(kl), _ptr(gr),
+                            0 if gr is None else gr.size, _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(delta), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd failed ({rc})")
+    return dq, dk, dv, delta
 
 
 def threads_used(nthreads: int = 0) -> int:

@@ -31,6 +31,9 @@
  * query head h attends with key/value head h / (H / Hkv) -- consecutive
  * query heads share one K/V head.  Hkv = H is ordinary multi-head attention.
  *
+ * The backward (gradients of this same attention for a given dO) is the
+ * chain rule written out term by term; see oracle_bwd.
+ *
  * Inputs are raw f16 / bf16 bit patterns; they are widened exactly to
  * double here.  All arithmetic is IEEE double, libm exp/log, no fast-math.
  */
@@ -251,6 +254,181 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtyp
             bad = -1;
         else if (bad >= 0)
             bad += jobs[t].bad;
+    }
+    free(jobs);
+    free(th);
+    return bad;
+}
+
+/* ------------------------------------------------------------ backward --- */
+
+/*
+ * Gradients of the attention above for a given output gradient dO (the
+ * gpu-inference page, section 02: the backward recomputes the probabilities
+ * and splits into a row term D, the K/V gradients and the Q gradient).  With
+ * P_ij the softmax probabilities of row i (zero for masked keys):
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = dO_i . O_i          (equal to sum_j P_ij dP_ij)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * dK and dV of a K/V head sum over the query heads that read it.  This is the
+ * chain rule through s_ij = scale q_i.k_j, the softmax and O = P V, written
+ * out term by term.
+ */
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    int dtype, B, H, Hkv, Nq, Nk, d, causal;
+    double scale;
+    const int32_t *kv_lens;
+    const int64_t *groups;   /* (b*Hkv + kvh) ids to compute, or NULL = all */
+    int64_t ngroups;
+    double *dq, *dk, *dv, *delta;
+    int nthreads, tid;
+    int bad;
+} bwd_job;
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job *J = (bwd_job *)arg;
+    const int d = J->d, Nq = J->Nq, Nk = J->Nk;
+    const int grp = J->H / J->Hkv;
+    double *kk = (double *)malloc(sizeof(double) * (size_t)Nk * d + 1);
+    double *vv = (double *)malloc(sizeof(double) * (size_t)Nk * d + 1);
+    double *qq = (double *)malloc(sizeof(double) * (size_t)d);
+    double *gg = (double *)malloc(sizeof(double) * (size_t)d);   /* dO row */
+    double *oo = (double *)malloc(sizeof(double) * (size_t)d);
+    double *p = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    if (!kk || !vv || !qq || !gg || !oo || !p) {
+        J->bad = -1;
+        goto done;
+    }
+    const int64_t total = J->groups ? J->ngroups : (int64_t)J->B * J->Hkv;
+    for (int64_t gi = J->tid; gi < total; gi += J->nthreads) {
+        const int64_t g = J->groups ? J->groups[gi] : gi;
+        const int b = (int)(g / J->Hkv);
+        const int64_t kvbase = g * Nk * d;
+        oracle_widen(J->k + kvbase, J->dtype, (int64_t)Nk * d, kk);
+        oracle_widen(J->v + kvbase, J->dtype, (int64_t)Nk * d, vv);
+        double *dk = J->dk + kvbase, *dv = J->dv + kvbase;
+        for (int64_t x = 0; x < (int64_t)Nk * d; ++x) {
+            dk[x] = 0.0;
+            dv[x] = 0.0;
+        }
+        int nb = J->kv_lens ? J->kv_lens[b] : Nk;
+        if (nb > Nk)
+            nb = Nk;
+        if (nb < 0)
+            nb = 0;
+        for (int h = (int)(g % J->Hkv) * grp; h < (int)(g % J->Hkv) * grp + grp; ++h) {
+            const int64_t bh = (int64_t)b * J->H + h;
+            for (int i = 0; i < Nq; ++i) {
+                const int64_t row = bh * Nq + i;
+                double *dq = J->dq + row * d;
+                int nvalid = nb;
+                if (J->causal) {
+                    int64_t lim = (int64_t)i + (Nk - Nq) + 1;
+                    if (lim < nvalid)
+                        nvalid = lim < 0 ? 0 : (int)lim;
+                }
+                for (int t = 0; t < d; ++t)
+                    dq[t] = 0.0;
+                J->delta[row] = 0.0;
+                if (nvalid <= 0)
+                    continue;
+                oracle_widen(J->q + row * d, J->dtype, d, qq);
+                oracle_widen(J->dout + row * d, J->dtype, d, gg);
+                /* probabilities (safe softmax of the masked score row) */
+                double m = -INFINITY;
+                for (int j = 0; j < nvalid; ++j) {
+                    double dot = 0.0;
+                    for (int t = 0; t < d; ++t)
+                        dot += qq[t] * kk[(int64_t)j * d + t];
+                    p[j] = J->scale * dot;
+                    if (p[j] > m)
+                        m = p[j];
+                }
+                double l = 0.0;
+                for (int j = 0; j < nvalid; ++j) {
+                    p[j] = exp(p[j] - m);
+                    l += p[j];
+                }
+                for (int t = 0; t < d; ++t)
+                    oo[t] = 0.0;
+                for (int j = 0; j < nvalid; ++j) {
+                    p[j] /= l;
+                    for (int t = 0; t < d; ++t)
+                        oo[t] += p[j] * vv[(int64_t)j * d + t];
+                }
+                /* D_i = dO_i . O_i */
+                double Di = 0.0;
+                for (int t = 0; t < d; ++t)
+                    Di += gg[t] * oo[t];
+                J->delta[row] = Di;
+                for (int j = 0; j < nvalid; ++j) {
+                    const double *vj = vv + (int64_t)j * d;
+                    const double *kj = kk + (int64_t)j * d;
+                    double dp = 0.0;
+                    for (int t = 0; t < d; ++t)
+                        dp += gg[t] * vj[t];
+                    const double ds = p[j] * (dp - Di);
+                    double *dkj = dk + (int64_t)j * d, *dvj = dv + (int64_t)j * d;
+                    for (int t = 0; t < d; ++t) {
+                        dq[t] += J->scale * ds * kj[t];
+                        dkj[t] += J->scale * ds * qq[t];
+                        dvj[t] += p[j] * gg[t];
+                    }
+                }
+            }
+        }
+    }
+done:
+    free(kk);
+    free(vv);
+    free(qq);
+    free(gg);
+    free(oo);
+    free(p);
+    return NULL;
+}
+
+/*
+ * Attention backward.  q, dout [B,H,Nq,d]; k, v [B,Hkv,Nk,d] (f16/bf16 bits).
+ * Writes dq [B,H,Nq,d], dk, dv [B,Hkv,Nk,d] and delta (D) [B,H,Nq] in double.
+ * groups: NULL for everything, else ngroups ids b*Hkv + kvh: only those K/V
+ * heads' dk/dv and the dq/delta rows of their query heads are written.
+ * Returns 0, -1 on allocation failure, -2 on bad head counts.
+ */
+int oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+               int dtype, int B, int H, int Hkv, int Nq, int Nk, int d, double scale,
+               int causal, const int32_t *kv_lens, const int64_t *groups, int64_t ngroups,
+               double *dq, double *dk, double *dv, double *delta, int nthreads)
+{
+    if (Hkv < 1 || H % Hkv != 0)
+        return -2;
+    const int64_t total = groups ? ngroups : (int64_t)B * Hkv;
+    int nt = thread_count(nthreads);
+    if ((int64_t)nt > total)
+        nt = total > 0 ? (int)total : 1;
+    bwd_job *jobs = (bwd_job *)calloc((size_t)nt, sizeof(bwd_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nt, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    for (int t = 0; t < nt; ++t) {
+        bwd_job J = {q, k, v, dout, dtype, B, H, Hkv, Nq, Nk, d, causal, scale, kv_lens,
+                     groups, ngroups, dq, dk, dv, delta, nt, t, 0};
+        jobs[t] = J;
+        pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
+    }
+    int bad = 0;
+    for (int t = 0; t < nt; ++t) {
+        pthread_join(th[t], NULL);
+        if (jobs[t].bad < 0)
+            bad = -1;
     }
     free(jobs);
     free(th);

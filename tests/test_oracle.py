@@ -439,3 +439,113 @@ def test_gqa_rejects_head_counts_that_do_not_divide():
         gen.fwd_inputs(1, 6, 4, 4, 8, "bf16", 0, causal=False, Hkv=4)
     with pytest.raises(ValueError):
         gen.decode_inputs(1, 6, 8, (1, 4), "bf16", 0, Hkv=4)
+
+
+# ------------------------------------------------------------- backward ---
+# Gradients of the attention for an output gradient dO (gpu-inference page,
+# section 02: row term D, dK/dV, dQ).  Pinned by central differences of an
+# independent numpy forward, and by closed forms and invariants.
+
+def _np_forward(q, k, v, scale, causal, kv_len=None):
+    """Plain numpy attention on float64 [N, d] arrays (definition only)."""
+    Nq, Nk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    n = Nk if kv_len is None else kv_len
+    mask = np.broadcast_to(np.arange(Nk)[None, :] < n, (Nq, Nk))
+    if causal:
+        mask = mask & (np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + Nk - Nq)
+    s = np.where(mask, s, -np.inf)
+    out = np.zeros((Nq, v.shape[1]))
+    for i in range(Nq):
+        if not mask[i].any():
+            continue
+        e = np.exp(s[i] - s[i][mask[i]].max())
+        out[i] = (e / e.sum()) @ v
+    return out
+
+
+@pytest.mark.parametrize("causal,kv_len,Nq,Nk", [(False, None, 5, 6), (True, None, 6, 6),
+                                                 (True, 4, 4, 7), (True, None, 7, 4),
+                                                 (False, 3, 5, 6)])
+def test_backward_matches_finite_differences(causal, kv_len, Nq, Nk):
+    rng = np.random.default_rng(70 + Nq + 10 * Nk + causal)
+    d, scale = 4, 0.7
+    q = _draw(rng, (1, 1, Nq, d), "bf16")
+    k = _draw(rng, (1, 1, Nk, d), "bf16")
+    v = _draw(rng, (1, 1, Nk, d), "bf16")
+    g = _draw(rng, (1, 1, Nq, d), "bf16")
+    kl = None if kv_len is None else np.array([kv_len], np.int32)
+    dq, dk, dv, delta = oracle.attention_bwd(q, k, v, g, "bf16", scale, causal, kl)
+    qf, kf, vf, gf = (_f(x, "bf16")[0, 0] for x in (q, k, v, g))
+
+    def loss(qx, kx, vx):
+        return float(np.sum(gf * _np_forward(qx, kx, vx, scale, causal, kv_len)))
+
+    h = 1e-6
+    for name, x, grad in (("q", qf, dq[0, 0]), ("k", kf, dk[0, 0]), ("v", vf, dv[0, 0])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, kf, vf), "k": (qf, xp, vf), "v": (qf, kf, xp)}[name]
+            args_m = {"q": (xm, kf, vf), "k": (qf, xm, vf), "v": (qf, kf, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.max(np.abs(fd - grad)) <= 1e-7, name
+    # the row term is dO . O
+    o = _np_forward(qf, kf, vf, scale, causal, kv_len)
+    np.testing.assert_allclose(delta[0, 0], np.sum(gf * o, axis=1), atol=1e-13, rtol=0)
+
+
+def test_backward_constant_v_gives_zero_q_and_k_gradients():
+    rng = np.random.default_rng(80)
+    q = _draw(rng, (1, 2, 9, 8), "bf16")
+    k = _draw(rng, (1, 2, 11, 8), "bf16")
+    row = _draw(rng, (1, 2, 1, 8), "bf16")
+    v = np.repeat(row, 11, axis=2)
+    g = _draw(rng, (1, 2, 9, 8), "bf16")
+    dq, dk, dv, delta = oracle.attention_bwd(q, k, v, g, "bf16", 0.5, True)
+    # O_i = v for every row, so dP_ij = dO_i . v = D_i and dS = 0
+    assert np.max(np.abs(dq)) <= 1e-13 and np.max(np.abs(dk)) <= 1e-13
+    np.testing.assert_allclose(delta[0], np.einsum("hid,hd->hi", _f(g, "bf16")[0],
+                                                   _f(row, "bf16")[0, :, 0]), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """Rows of P sum to one: sum_j dV_j = sum_i dO_i over rows that see a key;
+    rows of dS sum to zero: sum_j dK_j = 0."""
+    w = gen.fwd_inputs(2, 3, 13, 17, 8, "f16", 81 + causal, causal=causal, kv_len_range=(1, 17))
+    g = gen.fwd_inputs(2, 3, 13, 17, 8, "f16", 91, causal=causal).q
+    dq, dk, dv, _ = oracle.attention_bwd(w.q, w.k, w.v, g, "f16", w.scale, causal, w.kv_lens)
+    gf = _f(g, "f16")
+    for b in range(2):
+        n = int(w.kv_lens[b])
+        seen = np.array([min(n, i + 17 - 13 + 1) if causal else n for i in range(13)]) > 0
+        np.testing.assert_allclose(dv[b].sum(axis=1), gf[b][:, seen].sum(axis=1), atol=1e-12)
+        np.testing.assert_allclose(dk[b].sum(axis=1), 0.0, atol=1e-12)
+        assert np.all(dq[b][:, ~seen] == 0)
+
+
+def test_backward_gqa_sums_the_group_of_mha_gradients():
+    w = gen.fwd_inputs(2, 6, 10, 12, 8, "bf16", 95, causal=True, Hkv=2)
+    g = gen.fwd_inputs(2, 6, 10, 12, 8, "bf16", 96, causal=True).q
+    dq, dk, dv, delta = oracle.attention_bwd(w.q, w.k, w.v, g, "bf16", w.scale, True)
+    kr, vr = np.repeat(w.k, 3, axis=1), np.repeat(w.v, 3, axis=1)
+    dq2, dk2, dv2, delta2 = oracle.attention_bwd(w.q, kr, vr, g, "bf16", w.scale, True)
+    np.testing.assert_allclose(dq, dq2, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(delta, delta2, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(dk, dk2.reshape(2, 2, 3, 12, 8).sum(axis=2), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv, dv2.reshape(2, 2, 3, 12, 8).sum(axis=2), atol=1e-12, rtol=0)
+
+
+def test_backward_group_subset_equals_full():
+    w = gen.fwd_inputs(2, 4, 9, 9, 8, "bf16", 97, causal=False, Hkv=2)
+    g = gen.fwd_inputs(2, 4, 9, 9, 8, "bf16", 98, causal=False).q
+    full = oracle.attention_bwd(w.q, w.k, w.v, g, "bf16", w.scale, False)
+    part = oracle.attention_bwd(w.q, w.k, w.v, g, "bf16", w.scale, False, groups=[3, 0])
+    # groups 0 = (b0, kv head 0) -> query heads 0, 1; 3 = (b1, kv head 1) -> 2, 3
+    assert np.array_equal(part[0][0, :2], full[0][0, :2]) and np.isnan(part[0][0, 2:]).all()
+    assert np.array_equal(part[0][1, 2:], full[0][1, 2:])
+    assert np.array_equal(part[1][0, 0], full[1][0, 0]) and np.array_equal(part[2][1, 1], full[2][1, 1])
+    assert np.isnan(part[1][0, 1]).all()
