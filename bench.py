@@ -19,6 +19,9 @@ Prints ONE JSON line.  ``value`` is forward TFLOP/s (nominal FLOPs
 peak; and
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 forward workload on the host cores (and reports the sample's parity).
+``backward`` times fa_bwd (D pass, dK/dV pass, dQ pass) on the headline
+shape outside the step: nominal FLOPs 2.5x the forward's (five products of
+the forward's size against two).
 ``variants`` times generalised forward launches outside the step (head dims
 32 / 96 / 128, [B, N, H, d] inputs with a bf16 O, 4 K/V heads) on the same
 causal B8 H16 N4096 shape, each against the bf16 MFMA peak.
@@ -80,7 +83,10 @@ def fwd_bytes(B, H, Nq, Nk, d, elem=2):
     return B * H * (Nq + 2 * Nk) * d * elem + B * H * Nq * d * 4 + B * H * Nq * 4
 
 
-def kernel_digest(sources=("fa_fwd.hip", "fa_common.h")):
+FWD_SOURCES = ("fa_fwd.hip", "fa_tile.h", "fa_common.h")
+
+
+def kernel_digest(sources=FWD_SOURCES):
     h = hashlib.sha256()
     for name in sources:
         with open(os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", name), "rb") as f:
@@ -91,7 +97,7 @@ def kernel_digest(sources=("fa_fwd.hip", "fa_common.h")):
 DEC_SOURCES = ("fa_decode.hip", "fa_common.h")
 
 
-def measured_traffic(path=TRAFFIC_FILE, sources=("fa_fwd.hip", "fa_common.h")):
+def measured_traffic(path=TRAFFIC_FILE, sources=FWD_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     if they were taken on a different version of the kernel sources."""
     try:
@@ -133,7 +139,7 @@ def record_traffic(d, copy_bytes):
         factor[c] = copy_bytes / (copy[0] * 1024.0)
     out = {}
     for label, run, match, path, sources in (
-            ("fwd", "fwd_", "fwd_kernel", TRAFFIC_FILE, ("fa_fwd.hip", "fa_common.h")),
+            ("fwd", "fwd_", "fwd_kernel", TRAFFIC_FILE, FWD_SOURCES),
             ("decode", "fwd_", "decode_", DEC_TRAFFIC_FILE, DEC_SOURCES),
             ("decode_gqa", "gqa_", "decode_", GQA_TRAFFIC_FILE, DEC_SOURCES)):
         if not os.path.isdir(os.path.join(d, run + "FETCH_SIZE")):
@@ -258,6 +264,35 @@ def time_variants(fa, dev, steps, warmup):
     return out
 
 
+def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
+    """fa_bwd on the headline forward's inputs, O and LSE, with a seeded N(0, 1)
+    output gradient; average launch time over `steps` (HIP events)."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(8000)
+    dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    fa.forward(q, k, v, scale=w.scale, causal=w.causal, out=(o, lse))
+    outs = (torch.empty_like(o), torch.empty(k.shape, dtype=torch.float32, device=dev),
+            torch.empty(v.shape, dtype=torch.float32, device=dev), torch.empty_like(lse))
+    for _ in range(warmup):
+        fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 2.5 * attention_flops(B, H, Nq, Nk, d, w.causal)
+    tf = flops / (ms / 1e3) / 1e12
+    return {"workload": FWD_WORKLOAD, "kernel_ms_avg": ms, "TFLOP/s": tf,
+            "frac": tf / PEAK_BF16_TFLOPS, "flops": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +304,8 @@ def main():
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the generalised forward launches timed after the steps")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward timed after the steps")
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -433,6 +470,9 @@ def main():
                          "frac": g_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic(GQA_TRAFFIC_FILE, DEC_SOURCES)},
         }
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        result["backward"] = time_backward(fa, dev, q, k, v, o, lse, w, args.steps, args.warmup)
     if not args.no_variants:
         print("[bench] forward variants", file=sys.stderr, flush=True)
         result["variants"] = time_variants(fa, dev, args.steps, args.warmup)

@@ -6,12 +6,12 @@ device memory and the current stream.  There is no CPU path: if the library
 is missing or no GPU is present, calls raise.
 
 Two layers:
-  * ``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_ex``, ``fa_decode_paged``,
+  * ``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_ex``, ``fa_bwd``, ``fa_decode_paged``,
     ``fa_decode_paged_gqa``, ``fa_decode_workspace_bytes``, ``fa_status_str``,
     ``fa_last_hip_error``: the C entry points with the same names and
     arguments (raw device addresses as ints, stream as int, strides as
     3-tuples or None).
-  * ``forward`` / ``decode_paged``: take torch tensors, check them, allocate
+  * ``forward`` / ``backward`` / ``decode_paged``: take torch tensors, check them, allocate
     the outputs (and the decode workspace), call the entry point on the
     current stream and raise ``FAError`` on a non-zero status.  The number
     of K/V heads is read from k (or the pools); fewer K/V heads than query
@@ -41,7 +41,7 @@ FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F32 = 2
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_decode_paged", "fa_decode_paged_gqa",
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_bwd", "fa_decode_paged", "fa_decode_paged_gqa",
             "fa_decode_workspace_bytes", "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -93,6 +93,8 @@ def load_library():
     S3 = ctypes.POINTER(ctypes.c_int64)
     lib.fa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, F, I, P, I, I, P]
     lib.fa_fwd_ex.restype = I
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
+    lib.fa_bwd.restype = I
     lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode_paged.restype = I
     lib.fa_decode_paged_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
@@ -135,6 +137,12 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, q_strides, k_strides, v_st
                                     _strides3(k_strides), _strides3(v_strides),
                                     _strides3(o_strides), scale, causal, kv_lens, dtype, o_dtype,
                                     stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, d, scale, causal,
+           kv_lens, dtype, stream) -> int:
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, d,
+                                 scale, causal, kv_lens, dtype, stream)
 
 
 def fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
@@ -267,6 +275,53 @@ def forward(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
     if st != FA_OK:
         raise FAError(st, name)
     return o, lse
+
+
+def backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False,
+             kv_lens=None, stream=None, out=None):
+    """Gradients of the forward: q, dout [B, H, Nq, d]; k, v [B, H_kv, Nk, d]
+    (f16/bf16, contiguous); o [B, H, Nq, d] and lse [B, H, Nq] float32 from
+    the forward on the same inputs.  Returns (dq, dk, dv) float32 (dk, dv
+    summed over the query heads sharing a K/V head) and the row term delta.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        _check_dev(name, t)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("k, v must be [B, H_kv, Nk, d] and dout [B, H, Nq, d]")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the query heads must be a multiple of the K/V heads")
+    if o.dtype != torch.float32 or tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("o must be float32 [B, H, Nq, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("q, k, v, dout must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl_ptr = None
+    if kv_lens is not None:
+        _check_dev("kv_lens", kv_lens)
+        if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+            raise ValueError("kv_lens must be int32 [B]")
+        kl_ptr = kv_lens.data_ptr()
+    if out is None:
+        dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device)
+        dv = torch.empty_like(dk)
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, delta = out
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B,
+                H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt,
+                _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv, delta
 
 
 def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[float] = None,

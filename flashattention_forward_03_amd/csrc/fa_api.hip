@@ -137,6 +137,43 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
     return fa_fwd_gqa(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, kv_lens, dtype, stream);
 }
 
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const void *dout, const float *lse,
+           float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int Nq, int Nk, int d,
+           float scale, int causal, const int32_t *kv_lens, int dtype, void *stream)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+        return FA_ERR_SHAPE;
+    if (H > 0 && (H_kv < 1 || H % H_kv != 0))
+        return FA_ERR_SHAPE;
+    if (d != 64)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1)
+        return FA_ERR_ARG;
+    if (!scale_ok(scale))
+        return FA_ERR_ARG;
+    if (B == 0 || H == 0 || (Nq == 0 && Nk == 0))
+        return FA_OK;
+    if (fa::bwd_grid_size(B, H, Nq, Nk) > INT_MAX)
+        return FA_ERR_SHAPE;
+    // rows of one (b, head) are addressed with 32-bit byte offsets
+    if (((long long)(Nq > Nk ? Nq : Nk) + 64) * d * 2 > INT_MAX)
+        return FA_ERR_SHAPE;
+    if ((Nq > 0 && (!q || !o || !dout || !lse || !dq || !delta)) || (Nk > 0 && (!k || !v || !dk || !dv)))
+        return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4) ||
+        !aligned(kv_lens, 4))
+        return FA_ERR_ALIGN;
+    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, scale, causal == 1,
+                  dtype == FA_DTYPE_BF16, kv_lens};
+    const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_bwd launch");
+    return FA_OK;
+}
+
 size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size)
 {
     if (S < 0 || H < 0 || (d != 64 && d != 128) || max_pages_per_seq < 1 || page_size != 16)

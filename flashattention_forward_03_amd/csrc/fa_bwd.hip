@@ -1,0 +1,466 @@
+// Exact attention backward for gfx950 (MI355X).
+//
+// Method (gpu-inference page, section 02): the probabilities are recomputed
+// from the forward's saved log-sum-exp instead of being stored, and the work
+// splits into three kernels: a row term D_i = dO_i . O_i, a pass that owns a
+// block of keys and accumulates dK and dV over the query rows that see them,
+// and a pass that owns a block of query rows and accumulates dQ over their
+// keys.  With P_ij = exp(scale q_i.k_j - LSE_i) (zero where masked):
+//   dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i),
+//   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
+// Every gradient is written once by the block that owns it (no atomics), so
+// results are bitwise reproducible.  dK and dV of a K/V head sum over the
+// query heads that share it (grouped-query attention).
+//
+// gfx950 mapping (d = 64), both passes on the 32x32x16 MFMA with the same
+// register chaining as the forward (an accumulator's registers are the next
+// MFMA's B operand once the rows of the first product are permuted by sigma):
+//   * dQ pass: a workgroup = 4 waves x 32 query rows; Q and dO rows are held
+//     as B operands; K and V tiles of 32 keys stream through a three-slot LDS
+//     ring (buffer-to-LDS copies).  Per tile: S^T = K Q^T, dP^T = V dO^T,
+//     P^T and dS^T lane-local (each lane owns a query row, so LSE_i and D_i
+//     are per-lane scalars), then dQ^T += K^T dS^T with K^T read by the
+//     transposing LDS read.
+//   * dK/dV pass: a workgroup = 4 waves x 32 keys; K and V rows are held as B
+//     operands; Q and dO tiles of 32 rows, and their LSE and D values, stream
+//     through the ring.  Per tile: S = Q K^T and dP = dO V^T with a lane
+//     owning a key column, P and dS with the rows' LSE / D read from LDS,
+//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+#include "fa_common.h"
+#include "fa_internal.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace {
+
+constexpr int BWD_D = 64;      // head dim of the backward kernels
+constexpr int BQ = 128;        // query rows per dQ workgroup (32 per wave)
+constexpr int BK = 128;        // keys per dK/dV workgroup (32 per wave)
+constexpr int BT = 32;         // rows per streamed tile
+constexpr int STAGES = 3;      // LDS ring depth (tiles)
+
+// ---------------------------------------------------------------- D pass ---
+
+// delta[r] = sum_t dO[r, t] * O[r, t]; d/8 lanes per row, 8 head dims each.
+template <int D, bool BF16>
+__global__ __launch_bounds__(NTHREADS) void bwd_delta_kernel(const float *__restrict__ O,
+                                                             const uint16_t *__restrict__ dO,
+                                                             float *__restrict__ delta, long long rows)
+{
+    constexpr int TPR = D / 8;
+    const long long row = (long long)blockIdx.x * (NTHREADS / TPR) + threadIdx.x / TPR;
+    const int gd = threadIdx.x % TPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const f32x4_t o0 = *reinterpret_cast<const f32x4_t *>(O + row * D + 8 * gd);
+        const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(O + row * D + 8 * gd + 4);
+        const u32x4_t g = load16(dO + row * D + 8 * gd);
+        acc = o0[0] * lo16<BF16>(g[0]) + o0[1] * hi16<BF16>(g[0]) + o0[2] * lo16<BF16>(g[1]) +
+              o0[3] * hi16<BF16>(g[1]) + o1[0] * lo16<BF16>(g[2]) + o1[1] * hi16<BF16>(g[2]) +
+              o1[2] * lo16<BF16>(g[3]) + o1[3] * hi16<BF16>(g[3]);
+    }
+    acc = TPR == 16 ? row16_sum(acc) : row8_sum(acc);
+    if (row < rows && gd == 0)
+        delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dQ pass ---
+
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS, 3) void bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
+    float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int n_qtiles, float c_log2, float scale,
+    int causal_flag, const int32_t *__restrict__ kv_lens)
+{
+    constexpr int D = BWD_D;
+    using G = Geometry<D>;
+    static_assert(G::BN == BT, "tile rows");
+    constexpr int PER = 2 * G::PIECES_PER_WAVE;   // copies per lane per tile (K + V)
+    __shared__ __attribute__((aligned(1024))) unsigned char kring[STAGES][G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char vring[STAGES][G::TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const bool causal = causal_flag != 0;
+
+    // heaviest query tiles first (as the forward), heads contiguous per XCD
+    const int BHn = gridDim.x / n_qtiles;
+    const int slot = blockIdx.x % BHn;
+    const int bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);
+    const int qt = causal ? n_qtiles - 1 - blockIdx.x / BHn : blockIdx.x / BHn;
+    const int b = bhi / H, h = bhi - b * H;
+    const int kvh = h / (H / Hkv);
+    int kvlen = Nk;
+    if (kv_lens) {
+        kvlen = kv_lens[b];
+        kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
+    }
+    const size_t qbase = (size_t)bhi * Nq;
+    const uint16_t *Kb = K + ((size_t)b * Hkv + kvh) * Nk * D;
+    const uint16_t *Vb = V + ((size_t)b * Hkv + kvh) * Nk * D;
+
+    const int q0 = qt * BQ;
+    const int dq = Nk - Nq;
+    const int wave_first_row = q0 + wave * 32;
+    int key_end = kvlen, wave_key_end = kvlen;
+    if (causal) {
+        key_end = min(key_end, max(min(q0 + BQ, Nq) - 1 + dq + 1, 0));
+        wave_key_end = min(wave_key_end, max(min(wave_first_row + 32, Nq) - 1 + dq + 1, 0));
+    }
+    const int n_tiles = (key_end + BT - 1) / BT;
+    const int wave_tiles = min(n_tiles, (wave_key_end + BT - 1) / BT);
+    const int qrow = wave_first_row + l32;
+    int lim = kvlen;
+    if (causal)
+        lim = min(lim, qrow + dq + 1);
+
+    const u32x4s_t krs = make_rsrc(Kb, Nk * G::ROWB), vrs = make_rsrc(Vb, Nk * G::ROWB);
+    unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE], kstep[G::PIECES_PER_WAVE],
+        vstep[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, koff, kstep);   // both tiles are read by rows
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, voff, vstep);
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+        if (i < n_tiles) {
+            dma_tile<D>(krs, koff, kstep, G::ROWB, i * BT, kring[i], wave);
+            dma_tile<D>(vrs, voff, vstep, G::ROWB, i * BT, vring[i], wave);
+        }
+
+    // Q and dO rows of this lane's query (B operands), its LSE and D
+    u32x4_t qf[G::KSTEPS], gf[G::KSTEPS];
+    float lse2 = INFINITY, Di = 0.f;   // lse2 = +inf makes P = 0 (rows past Nq, rows without keys)
+    {
+        const bool ok = qrow < Nq;
+        const size_t r = qbase + (ok ? qrow : 0);
+        const uint16_t *qp = Q + r * D + 8 * hh;
+        const uint16_t *gp = dO + r * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c) {
+            qf[c] = ok ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
+            gf[c] = ok ? load16(gp + 16 * c) : u32x4_t{0, 0, 0, 0};
+        }
+        if (ok) {
+            const float l = LSE[r];
+            if (l > -INFINITY)
+                lse2 = l * kLog2e;
+            Di = delta[r];
+        }
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c) {
+            asm volatile("" : "+v"(qf[c]));
+            asm volatile("" : "+v"(gf[c]));
+        }
+        asm volatile("" : "+v"(lse2), "+v"(Di));
+    }
+
+    f32x16_t acc[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+        acc[db] = f32x16_t{};
+    const int krow = sigma(l32);
+
+    auto iter = [&](int t, int cur, int fill) {
+        if (t + STAGES - 2 < n_tiles)
+            wait_vmcnt<(STAGES - 2) * PER>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (t + STAGES - 1 < n_tiles) {
+            dma_tile<D>(krs, koff, kstep, G::ROWB, (t + STAGES - 1) * BT, kring[fill], wave);
+            dma_tile<D>(vrs, voff, vstep, G::ROWB, (t + STAGES - 1) * BT, vring[fill], wave);
+        }
+        if (t < wave_tiles) {
+            const int kt0 = t * BT;
+            f32x16_t s[1], dp[1];
+            qk_tile<D, BF16>(kring[cur], krow, hh, qf, s);    // S^T = K Q^T
+            qk_tile<D, BF16>(vring[cur], krow, hh, gf, dp);   // dP^T = V dO^T
+            __builtin_amdgcn_sched_barrier(0);
+            if ((kt0 + BT > kvlen) || (causal && kt0 + BT - 1 > wave_first_row + dq))
+                mask_tile<D>(s, lim - (kt0 + 8 * hh));
+            // P^T and dS^T, packed to 16 bits as the B operand of dQ^T += K^T dS^T
+            u32x4_t dsf[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = 8 * h2 + 2 * q;
+                    const float p0 = fast_exp2(fmaf(s[0][r], c_log2, -lse2));
+                    const float p1 = fast_exp2(fmaf(s[0][r + 1], c_log2, -lse2));
+                    dsf[h2][q] = pack2<BF16>(p0 * (dp[0][r] - Di), p1 * (dp[0][r + 1] - Di));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4_t ka[G::DB][G::PCH];
+            pv_operands<D, true>(kring[cur], lane, hh, ka);   // K^T
+            pv_mfma<D, BF16>(ka, dsf, acc);
+        }
+    };
+    int t = 0;
+    for (; t + 2 < n_tiles; t += 3) {
+        iter(t, 0, 2);
+        iter(t + 1, 1, 0);
+        iter(t + 2, 2, 1);
+    }
+    if (t < n_tiles)
+        iter(t, 0, 2);
+    if (t + 1 < n_tiles)
+        iter(t + 1, 1, 0);
+    __syncthreads();
+
+    if (qrow < Nq) {
+        float *op = dQ + (qbase + qrow) * D + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4_t *>(op + 32 * db + 8 * g) =
+                    f32x4_t{acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                            acc[db][4 * g + 3] * scale};
+    }
+}
+
+// ------------------------------------------------------------- dK/dV pass ---
+
+// Copy 32 consecutive fp32 values (a tile's LSE or D) into this wave's LDS
+// slot: lanes 0..31 load one dword each, lanes 32..63 read out of range
+// (zero) into the slot's unused half.
+__device__ __forceinline__ void dma_rows32(const u32x4s_t &rsrc, int r0, unsigned char *dst, int lane)
+{
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)dst);
+    const uint32_t voff = lane < 32 ? (unsigned)(r0 + lane) * 4u : kOutOfRange;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_addr), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
+    float *__restrict__ dK, float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int n_ktiles, float c_log2,
+    float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
+{
+    constexpr int D = BWD_D;
+    using G = Geometry<D>;
+    static_assert(G::BN == BT, "tile rows");
+    constexpr int PER = 2 * G::PIECES_PER_WAVE + 2;   // Q, dO pieces + LSE, D rows
+    __shared__ __attribute__((aligned(1024))) unsigned char qring[STAGES][G::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char gring[STAGES][G::TILE];
+    __shared__ __attribute__((aligned(256))) unsigned char sring[STAGES][4][2][256];   // per wave: LSE, D
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const bool causal = causal_flag != 0;
+
+    // lowest key tiles first (they have the most query rows when causal)
+    const int BHn = gridDim.x / n_ktiles;
+    const int slot = blockIdx.x % BHn;
+    const int g = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);   // b * Hkv + kvh
+    const int kt = blockIdx.x / BHn;
+    const int b = g / Hkv, kvh = g - b * Hkv;
+    const int grp = H / Hkv;
+    int kvlen = Nk;
+    if (kv_lens) {
+        kvlen = kv_lens[b];
+        kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
+    }
+    const int dq = Nk - Nq;
+    const int k0 = kt * BK;
+    const int kw0 = k0 + wave * 32;   // this wave's first key
+    const int key = kw0 + l32;        // this lane's key (accumulator column)
+
+    // query tiles that see any key of the workgroup, per query head
+    int qt_begin = 0;
+    if (causal)
+        qt_begin = max(0, k0 - dq) / BT;
+    int n_qt = (Nq + BT - 1) / BT - qt_begin;
+    if (k0 >= kvlen || (causal && k0 - dq > Nq - 1))
+        n_qt = 0;
+    const int n_tiles = n_qt > 0 ? n_qt * grp : 0;   // (query head, query tile) pairs
+
+    // K and V rows of this lane's key (B operands)
+    u32x4_t kf[G::KSTEPS], vf[G::KSTEPS];
+    {
+        const bool ok = key < Nk;
+        const size_t r = ((size_t)g * Nk + (ok ? key : 0)) * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c) {
+            kf[c] = ok ? load16(K + r + 16 * c) : u32x4_t{0, 0, 0, 0};
+            vf[c] = ok ? load16(V + r + 16 * c) : u32x4_t{0, 0, 0, 0};
+        }
+    }
+
+    unsigned qoff[G::PIECES_PER_WAVE], goff[G::PIECES_PER_WAVE], qstep[G::PIECES_PER_WAVE],
+        gstep[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff, qstep);
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, goff, gstep);
+    auto issue = [&](int i, int st) {   // copy (query head, tile) pair i into ring slot st
+        const int hq = kvh * grp + i / n_qt;
+        const int r0 = (qt_begin + i % n_qt) * BT;
+        const size_t rowbase = ((size_t)b * H + hq) * Nq;
+        const u32x4s_t qrs = make_rsrc(Q + rowbase * D, Nq * G::ROWB);
+        const u32x4s_t grs = make_rsrc(dO + rowbase * D, Nq * G::ROWB);
+        const u32x4s_t lrs = make_rsrc(LSE + rowbase, Nq * 4);
+        const u32x4s_t drs = make_rsrc(delta + rowbase, Nq * 4);
+        dma_tile<D>(qrs, qoff, qstep, G::ROWB, r0, qring[st], wave);
+        dma_tile<D>(grs, goff, gstep, G::ROWB, r0, gring[st], wave);
+        dma_rows32(lrs, r0, sring[st][wave][0], lane);
+        dma_rows32(drs, r0, sring[st][wave][1], lane);
+    };
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+        if (i < n_tiles)
+            issue(i, i);
+#pragma unroll
+    for (int c = 0; c < G::KSTEPS; ++c) {
+        asm volatile("" : "+v"(kf[c]));
+        asm volatile("" : "+v"(vf[c]));
+    }
+
+    f32x16_t dkacc[G::DB], dvacc[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        dkacc[db] = f32x16_t{};
+        dvacc[db] = f32x16_t{};
+    }
+    const int qrow_perm = sigma(l32);
+    const int lim_key = min(kvlen, Nk);
+
+    auto iter = [&](int t, int cur, int fill) {
+        if (t + STAGES - 2 < n_tiles)
+            wait_vmcnt<(STAGES - 2) * PER>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (t + STAGES - 1 < n_tiles)
+            issue(t + STAGES - 1, fill);
+        const int q0 = (qt_begin + t % n_qt) * BT;
+        // wave-uniform: does any query of this tile see any key of this wave?
+        const bool live = kw0 < lim_key && (!causal || kw0 <= q0 + BT - 1 + dq);
+        if (live) {
+            f32x16_t s[1], dp[1];
+            qk_tile<D, BF16>(qring[cur], qrow_perm, hh, kf, s);    // S = Q K^T
+            qk_tile<D, BF16>(gring[cur], qrow_perm, hh, vf, dp);   // dP = dO V^T
+            __builtin_amdgcn_sched_barrier(0);
+            // this lane's rows: register r is query q0 + 16*(r/8) + 8*hh + r%8
+            const float *ls = reinterpret_cast<const float *>(sring[cur][wave][0]);
+            const float *ds = reinterpret_cast<const float *>(sring[cur][wave][1]);
+            // wave-uniform: may any element of this block be masked?
+            const bool edge = kw0 + 32 > lim_key || q0 + BT > Nq || (causal && kw0 + 31 > q0 + dq);
+            u32x4_t pf[2], dsf[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4_t la = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh);
+                const f32x4_t lb = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh + 4);
+                const f32x4_t da = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh);
+                const f32x4_t dbv = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh + 4);
+                float p[8], dsv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * h2 + e;
+                    const float lse = e < 4 ? la[e] : lb[e - 4];
+                    const float dd = e < 4 ? da[e] : dbv[e - 4];
+                    float pe = fast_exp2(fmaf(s[0][r], c_log2, -lse * kLog2e));
+                    if (edge) {
+                        const int qi = q0 + 16 * h2 + 8 * hh + e;
+                        const bool vis = key < lim_key && qi < Nq && (!causal || key <= qi + dq);
+                        pe = vis ? pe : 0.f;
+                    }
+                    p[e] = pe;
+                    dsv[e] = pe * (dp[0][r] - dd);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pf[h2][q] = pack2<BF16>(p[2 * q], p[2 * q + 1]);
+                    dsf[h2][q] = pack2<BF16>(dsv[2 * q], dsv[2 * q + 1]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4_t ta[G::DB][G::PCH];
+            pv_operands<D, true>(gring[cur], lane, hh, ta);   // dO^T
+            pv_mfma<D, BF16>(ta, pf, dvacc);                  // dV^T += dO^T P
+            __builtin_amdgcn_sched_barrier(0);
+            pv_operands<D, true>(qring[cur], lane, hh, ta);   // Q^T
+            pv_mfma<D, BF16>(ta, dsf, dkacc);                 // dK^T += Q^T dS
+        }
+    };
+    int t = 0;
+    for (; t + 2 < n_tiles; t += 3) {
+        iter(t, 0, 2);
+        iter(t + 1, 1, 0);
+        iter(t + 2, 2, 1);
+    }
+    if (t < n_tiles)
+        iter(t, 0, 2);
+    if (t + 1 < n_tiles)
+        iter(t + 1, 1, 0);
+    __syncthreads();
+
+    if (key < Nk) {
+        const size_t r = ((size_t)g * Nk + key) * D + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                *reinterpret_cast<f32x4_t *>(dK + r + 32 * db + 8 * q) =
+                    f32x4_t{dkacc[db][4 * q] * scale, dkacc[db][4 * q + 1] * scale, dkacc[db][4 * q + 2] * scale,
+                            dkacc[db][4 * q + 3] * scale};
+                *reinterpret_cast<f32x4_t *>(dV + r + 32 * db + 8 * q) =
+                    f32x4_t{dvacc[db][4 * q], dvacc[db][4 * q + 1], dvacc[db][4 * q + 2], dvacc[db][4 * q + 3]};
+            }
+    }
+}
+
+template <bool BF16>
+hipError_t launch(const BwdArgs &a, hipStream_t stream)
+{
+    constexpr int D = BWD_D;
+    const long long rows = (long long)a.B * a.H * a.Nq;
+    const int rows_per_wg = NTHREADS / (D / 8);
+    hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
+                       dim3(NTHREADS), 0, stream, a.o, (const uint16_t *)a.dout, a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const float c_log2 = a.scale * kLog2e;
+    const int n_ktiles = (a.Nk + BK - 1) / BK;
+    if (n_ktiles > 0) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
+                           dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                           (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse, a.delta, a.dk, a.dv, a.H,
+                           a.Hkv, a.Nq, a.Nk, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int n_qtiles = (a.Nq + BQ - 1) / BQ;
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
+                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (const uint16_t *)a.dout, a.lse, a.delta, a.dq, a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, c_log2,
+                       a.scale, a.causal ? 1 : 0, a.kv_lens);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+long long bwd_grid_size(int B, int H, int Nq, int Nk)
+{
+    const long long a = (long long)((Nq + BQ - 1) / BQ) * B * H;
+    const long long c = (long long)((Nk + BK - 1) / BK) * B * H;
+    const long long r = ((long long)B * H * Nq + 7) / 8;
+    return a > c ? (a > r ? a : r) : (c > r ? c : r);
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
+{
+    return a.bf16 ? launch<true>(a, stream) : launch<false>(a, stream);
+}
+
+}  // namespace fa

@@ -48,25 +48,6 @@ constexpr int NTHREADS = 256;
 constexpr int STEPS_IN_FLIGHT = 16;  // wave steps loaded before any is used
 constexpr int GROUP = NTHREADS / 64;  // heads per workgroup, one per wave
 
-// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), result in all of them.
-__device__ __forceinline__ float row16_sum(float x)
-{
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // row_half_mirror
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row_mirror
-    return x;
-}
-
-// Sum over aligned groups of 8 lanes.
-__device__ __forceinline__ float row8_sum(float x)
-{
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-    return x;
-}
-
 template <bool BF16>
 __device__ __forceinline__ void widen8(const u32x4_t &w, float *f)
 {

@@ -46,6 +46,20 @@ struct DecodeArgs {
 long long fwd_grid_size(int B, int H, int Nq);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
+// Backward (contiguous [B, heads, N, d] tensors, d = 64): D = rowsum(dO * O)
+// into delta, then dK/dV and dQ.
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *o, *lse;
+    float *dq, *dk, *dv, *delta;
+    int B, H, Hkv, Nq, Nk;
+    float scale;
+    bool causal, bf16;
+    const int32_t *kv_lens;
+};
+long long bwd_grid_size(int B, int H, int Nq, int Nk);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
 // Decode: cached tokens per split-KV chunk, and the launch.
 constexpr int kDecodeChunkPages = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }

@@ -3,7 +3,7 @@
  *
  * Two operations, both asynchronous on the caller's HIP stream (each also with
  * grouped-query heads, the _gqa calls; the forward also with strides and a
- * 16-bit O, fa_fwd_ex):
+ * 16-bit O, fa_fwd_ex), and the forward's backward (fa_bwd):
  *
  *   fa_fwd           exact attention forward: O = softmax(scale * Q K^T + mask) V
  *                    and the per-row log-sum-exp, computed tile by tile with an
@@ -141,6 +141,36 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
               const int64_t *k_strides, const int64_t *v_strides, const int64_t *o_strides,
               float scale, int causal, const int32_t *kv_lens, int dtype, int o_dtype,
               void *stream);
+
+/*
+ * Exact attention backward from the forward's saved log-sum-exp (gpu-inference
+ * page, section 02: the probabilities are recomputed, not stored; three
+ * passes: the row term D, then dK/dV, then dQ).  With P the forward's masked
+ * softmax probabilities and dout = dL/dO:
+ *   delta[i] = D_i = dO_i . O_i
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j.
+ *
+ *   q, dout  [B, H, Nq, d] f16/bf16 (dtype), contiguous; 16-byte aligned
+ *   k, v     [B, H_kv, Nk, d] same dtype (H a multiple of H_kv); 16-byte aligned
+ *   o        [B, H, Nq, d] float32: the forward's O for these inputs; 16-byte aligned
+ *   lse      [B, H, Nq] float32: the forward's LSE; 4-byte aligned
+ *   dq       [B, H, Nq, d] float32 output; 16-byte aligned
+ *   dk, dv   [B, H_kv, Nk, d] float32 outputs (summed over the query heads that
+ *            share each K/V head); 16-byte aligned
+ *   delta    [B, H, Nq] float32, written with D (caller-owned scratch that the
+ *            dK/dV and dQ passes read); 4-byte aligned
+ *   d        64 (other head dims: FA_ERR_UNSUPPORTED)
+ *   scale, causal, kv_lens: as for the forward that produced o and lse.
+ *
+ * Rows with no valid key get dQ = 0; keys no row sees get dK = dV = 0.  Every
+ * output element is written by exactly one block (no atomics): results are
+ * bitwise reproducible.  (max(Nq, Nk) + 64) * d * 2 must stay below 2^31.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const void *dout,
+           const float *lse, float *dq, float *dk, float *dv, float *delta, int B, int H,
+           int H_kv, int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens,
+           int dtype, void *stream);
 
 /*
  * Decode attention over a paged KV cache (query length 1).

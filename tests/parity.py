@@ -75,3 +75,28 @@ def sample_rows(B, H, Nq, n_random, seed, full_heads=((0, 0),), edge=128):
         rows.extend(range(base + max(0, Nq - edge), base + Nq))
     rows.extend(rng.integers(0, B * H * Nq, size=n_random).tolist())
     return np.unique(np.array(rows, np.int64))
+
+
+# Gradients (dQ, dK, dV, and the row term D): the bar of the gpu-inference
+# page's backward checks (section 02: every gradient held to the reference
+# with allclose at atol = rtol = 1e-2), elementwise: |x - ref| <= 1e-2 +
+# 1e-2 |ref|.  No separate mean bar: each gradient element is a sum of
+# products with 16-bit-rounded factors (P and dS enter the MFMAs rounded),
+# so its error scales with the sum of |terms|, which cancellation can make
+# much larger than |ref|; the mean error is reported.
+GRAD_ATOL = 1e-2
+GRAD_RTOL = 1e-2
+
+
+def compare_grad(x, ref, what=""):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, f"{what}: shape {x.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(x)), f"{what}: non-finite values"
+    err = np.abs(x - ref)
+    excess = err - (GRAD_ATOL + GRAD_RTOL * np.abs(ref))
+    worst = float(excess.max(initial=-np.inf))
+    stats = dict(max_abs=float(err.max(initial=0.0)),
+                 mean_abs=float(err.mean()) if err.size else 0.0, worst_excess=worst)
+    assert worst <= 0.0, f"{what}: outside atol/rtol {stats}"
+    return stats

@@ -241,3 +241,34 @@ def call_fwd_ex(qs=None, ks=None, vs=None, os_=None, o_dtype=fa.FA_DTYPE_F32, H_
 ])
 def test_fwd_ex_argument_checks(lib, kw, status):
     assert call_fwd_ex(**kw) == status
+
+
+def call_bwd(**over):
+    a = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, delta=A, B=1, H=2, H_kv=1, Nq=8,
+             Nk=8, d=64, scale=0.125, causal=1, kv_lens=None, dtype=1, stream=None)
+    a.update(over)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["delta"], a["B"], a["H"], a["H_kv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                     a["causal"], a["kv_lens"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), fa.FA_ERR_SHAPE),
+    (dict(Nq=-1), fa.FA_ERR_SHAPE),
+    (dict(causal=3), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(Nk=(1 << 24)), fa.FA_ERR_SHAPE),
+    (dict(delta=None), fa.FA_ERR_NULL),
+    (dict(dk=None), fa.FA_ERR_NULL),
+    (dict(do=A + 8), fa.FA_ERR_ALIGN),
+    (dict(dv=A + 4), fa.FA_ERR_ALIGN),
+    (dict(lse=A + 2), fa.FA_ERR_ALIGN),
+    (dict(B=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None,
+          delta=None), fa.FA_OK),
+    (dict(Nq=0, Nk=0), fa.FA_OK),
+])
+def test_bwd_argument_checks(lib, over, status):
+    assert call_bwd(**over) == status

@@ -1,0 +1,84 @@
+"""GPU parity of the attention backward (fa_bwd through the binding) against the
+fp64 oracle's gradients: dQ, dK, dV and the row term D."""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as gen
+import oracle
+from parity import compare_grad, device_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, g_bits):
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    q, k, v, kl = device_tensors(w)
+    g = gen.to_torch(g_bits, w.dtype).cuda()
+    o, lse = fa.forward(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl)
+    dq, dk, dv, delta = fa.backward(q, k, v, o, lse, g, scale=w.scale, causal=w.causal,
+                                    kv_lens=kl)
+    torch.cuda.synchronize()
+    return tuple(x.cpu().numpy() for x in (dq, dk, dv, delta))
+
+
+def _dout(w, seed):
+    rng = np.random.default_rng(seed)
+    return gen.round_bits(rng.standard_normal(w.q.shape, dtype=np.float32), w.dtype)
+
+
+def _check(w, g, what, groups=None):
+    got = _run(w, g)
+    ref = oracle.attention_bwd(w.q, w.k, w.v, g, w.dtype, w.scale, w.causal, w.kv_lens,
+                               groups=groups)
+    out = {}
+    for name, x, r in zip(("dq", "dk", "dv", "delta"), got, ref):
+        sel = ~np.isnan(r)
+        out[name] = compare_grad(x[sel], r[sel], f"{what} {name}")
+    print(what, out, flush=True)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,dtype,causal,lens", [
+    (1, 2, 2, 128, 128, "bf16", True, None),
+    (2, 4, 2, 200, 200, "bf16", True, (50, 200)),     # grouped heads, padding
+    (2, 3, 3, 160, 300, "f16", False, None),           # Nq < Nk, ragged
+    (1, 2, 1, 300, 130, "bf16", True, None),           # Nq > Nk: leading rows see nothing
+    (1, 2, 2, 77, 333, "f16", True, None),             # bottom-right diagonal
+    (2, 2, 2, 1, 100, "bf16", False, (0, 100)),        # one query row; kv_len 0
+    (1, 1, 1, 64, 5, "bf16", False, None),             # Nk smaller than a tile
+    (2, 8, 1, 96, 96, "f16", True, None),              # multi-query
+])
+def test_backward_parity(B, H, Hkv, Nq, Nk, dtype, causal, lens):
+    w = gen.fwd_inputs(B, H, Nq, Nk, 64, dtype, seed=11000 + B * 100 + Nq + Nk, causal=causal,
+                       kv_len_range=lens, Hkv=Hkv)
+    _check(w, _dout(w, 11500 + Nq), f"bwd B{B} H{H}/{Hkv} Nq{Nq} Nk{Nk} {dtype} causal={causal} "
+                                    f"lens={lens}")
+
+
+def test_backward_constant_v():
+    """Equal V rows: O is that row everywhere, dS = 0, so dQ = dK = 0."""
+    w = gen.fwd_inputs(1, 2, 150, 150, 64, "bf16", seed=11600, causal=True)
+    w.v[:] = w.v[:, :, :1, :]
+    dq, dk, dv, _ = _run(w, _dout(w, 11601))
+    assert np.max(np.abs(dq)) <= 1e-2 and np.max(np.abs(dk)) <= 1e-2
+
+
+def test_backward_deterministic():
+    w = gen.fwd_inputs(2, 4, 300, 300, 64, "bf16", seed=11700, causal=True, Hkv=2)
+    g = _dout(w, 11701)
+    a = _run(w, g)
+    b = _run(w, g)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_full_size_sampled_heads():
+    """The causal B8 H16 N4096 d64 backward (the launch the bench times); the
+    oracle computes the full gradients of two (batch, head) pairs."""
+    w = gen.fwd_workload("fwd_causal_b8h16_n4096_d64_bf16")
+    g = _dout(w, 11800)
+    _check(w, g, "bwd full size", groups=[0, 8 * 16 - 1])
