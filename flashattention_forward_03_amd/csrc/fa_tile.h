@@ -186,9 +186,14 @@ __device__ __forceinline__ void pv_operands(const unsigned char *vb, int lane, i
         for (int c = 0; c < G::PCH; ++c) {
             const int r0 = 16 * c + 8 * hh + (j16 >> 2);
             const int r1 = r0 + 4;
-            const int s0 = KSWZ ? swz_k(r0) : swz_v(r0), s1 = KSWZ ? swz_k(r1) : swz_v(r1);
-            const unsigned char *a0 = vb + r0 * G::ROWB + (swz_slot<G::DC>(chunk, s0) << 4) + half;
-            const unsigned char *a1 = vb + r1 * G::ROWB + (swz_slot<G::DC>(chunk, s1) << 4) + half;
+            const unsigned char *a0, *a1;
+            if constexpr (KSWZ) {
+                a0 = vb + r0 * G::ROWB + (swz_slot<G::DC>(chunk, swz_k(r0)) << 4) + half;
+                a1 = vb + r1 * G::ROWB + (swz_slot<G::DC>(chunk, swz_k(r1)) << 4) + half;
+            } else {
+                a0 = vb + r0 * G::ROWB + (swz_slot<G::DC>(chunk, swz_v(r0)) << 4) + half;
+                a1 = vb + r1 * G::ROWB + (swz_slot<G::DC>(chunk, swz_v(r1)) << 4) + half;
+            }
             const u32x2_t y0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a0));
             const u32x2_t y1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a1));
             va[db][c] = u32x4_t{y0[0], y0[1], y1[0], y1[1]};
