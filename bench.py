@@ -22,6 +22,9 @@ forward workload on the host cores (and reports the sample's parity).
 ``backward`` times fa_bwd (D pass, dK/dV pass, dQ pass) on the headline
 shape outside the step: nominal FLOPs 2.5x the forward's (five products of
 the forward's size against two).
+``kv_append`` times fa_kv_append writing the whole grouped-query decode batch
+(every cached token's K and V rows) into its pages, against the 8 TB/s peak
+on the bytes read plus written.
 ``variants`` times generalised forward launches outside the step (head dims
 32 / 96 / 128, [B, N, H, d] inputs with a bf16 O, 4 K/V heads) on the same
 causal B8 H16 N4096 shape, each against the bf16 MFMA peak.
@@ -264,6 +267,34 @@ def time_variants(fa, dev, steps, warmup):
     return out
 
 
+def time_append(fa, dev, gq, kp, vp, pt, steps, warmup):
+    """fa_kv_append of every token of the grouped-query decode batch into its
+    pages (rewriting the pools with their own contents); average over `steps`
+    launches with HIP events.  Bytes: the new rows read plus the rows written."""
+    import torch
+
+    kn = gen.to_torch(gq.k, gq.dtype).to(dev)
+    vn = gen.to_torch(gq.v, gq.dtype).to(dev)
+    seq = torch.from_numpy(np.repeat(np.arange(gq.S, dtype=np.int32), gq.kv_lens)).to(dev)
+    pos = torch.from_numpy(np.concatenate([np.arange(n, dtype=np.int32)
+                                           for n in gq.kv_lens])).to(dev)
+    for _ in range(warmup):
+        fa.kv_append(kn, vn, seq, pos, kp, vp, pt)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fa.kv_append(kn, vn, seq, pos, kp, vp, pt)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    T = int(gq.kv_lens.sum())
+    nbytes = 2 * 2 * T * gq.Hkv * gq.d * 2 + 2 * T * 4 + T * 4   # K+V read and written; ids
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": GQA_WORKLOAD, "tokens": T, "kernel_ms_avg": ms, "bytes": nbytes,
+            "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+
 def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
     """fa_bwd on the headline forward's inputs, O and LSE, with a seeded N(0, 1)
     output gradient; average launch time over `steps` (HIP events)."""
@@ -306,6 +337,8 @@ def main():
                     help="skip the generalised forward launches timed after the steps")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward timed after the steps")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the paged-cache append timed after the steps")
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -473,6 +506,9 @@ def main():
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
         result["backward"] = time_backward(fa, dev, q, k, v, o, lse, w, args.steps, args.warmup)
+    if gq is not None and not args.no_append:
+        print("[bench] kv append", file=sys.stderr, flush=True)
+        result["kv_append"] = time_append(fa, dev, gq, g_kp, g_vp, g_pt, args.steps, args.warmup)
     if not args.no_variants:
         print("[bench] forward variants", file=sys.stderr, flush=True)
         result["variants"] = time_variants(fa, dev, args.steps, args.warmup)

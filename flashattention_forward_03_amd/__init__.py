@@ -11,7 +11,8 @@ Two layers:
     ``fa_last_hip_error``: the C entry points with the same names and
     arguments (raw device addresses as ints, stream as int, strides as
     3-tuples or None).
-  * ``forward`` / ``backward`` / ``decode_paged``: take torch tensors, check them, allocate
+  * ``Pager``: the host page allocator.
+  * ``forward`` / ``backward`` / ``decode_paged`` / ``kv_append``: take torch tensors, check them, allocate
     the outputs (and the decode workspace), call the entry point on the
     current stream and raise ``FAError`` on a non-zero status.  The number
     of K/V heads is read from k (or the pools); fewer K/V heads than query
@@ -37,11 +38,14 @@ FA_ERR_ALIGN = 4
 FA_ERR_WORKSPACE = 5
 FA_ERR_HIP = 6
 FA_ERR_ARG = 7
+FA_ERR_NOMEM = 8
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F32 = 2
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_bwd", "fa_decode_paged", "fa_decode_paged_gqa",
+            "fa_kv_append", "fa_pager_create", "fa_pager_destroy", "fa_pager_reserve",
+            "fa_pager_release", "fa_pager_length", "fa_pager_free_pages", "fa_pager_copy_table",
             "fa_decode_workspace_bytes", "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -95,6 +99,22 @@ def load_library():
     lib.fa_fwd_ex.restype = I
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P]
     lib.fa_bwd.restype = I
+    lib.fa_kv_append.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, P]
+    lib.fa_kv_append.restype = I
+    lib.fa_pager_create.argtypes = [I, I, I]
+    lib.fa_pager_create.restype = P
+    lib.fa_pager_destroy.argtypes = [P]
+    lib.fa_pager_destroy.restype = None
+    lib.fa_pager_reserve.argtypes = [P, I, I]
+    lib.fa_pager_reserve.restype = I
+    lib.fa_pager_release.argtypes = [P, I]
+    lib.fa_pager_release.restype = I
+    lib.fa_pager_length.argtypes = [P, I]
+    lib.fa_pager_length.restype = I
+    lib.fa_pager_free_pages.argtypes = [P]
+    lib.fa_pager_free_pages.restype = I
+    lib.fa_pager_copy_table.argtypes = [P, P, Z]
+    lib.fa_pager_copy_table.restype = I
     lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode_paged.restype = I
     lib.fa_decode_paged_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
@@ -143,6 +163,41 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, d, scal
            kv_lens, dtype, stream) -> int:
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, d,
                                  scale, causal, kv_lens, dtype, stream)
+
+
+def fa_kv_append(k_new, v_new, seq_ids, positions, T, k_pages, v_pages, page_table, S, H_kv, d,
+                 page_size, max_pages_per_seq, num_pages, dtype, stream) -> int:
+    return load_library().fa_kv_append(k_new, v_new, seq_ids, positions, T, k_pages, v_pages,
+                                       page_table, S, H_kv, d, page_size, max_pages_per_seq,
+                                       num_pages, dtype, stream)
+
+
+def fa_pager_create(num_pages, max_seqs, max_pages_per_seq):
+    return load_library().fa_pager_create(num_pages, max_seqs, max_pages_per_seq)
+
+
+def fa_pager_destroy(p) -> None:
+    load_library().fa_pager_destroy(p)
+
+
+def fa_pager_reserve(p, seq, length) -> int:
+    return load_library().fa_pager_reserve(p, seq, length)
+
+
+def fa_pager_release(p, seq) -> int:
+    return load_library().fa_pager_release(p, seq)
+
+
+def fa_pager_length(p, seq) -> int:
+    return load_library().fa_pager_length(p, seq)
+
+
+def fa_pager_free_pages(p) -> int:
+    return load_library().fa_pager_free_pages(p)
+
+
+def fa_pager_copy_table(p, dst, dst_entries) -> int:
+    return load_library().fa_pager_copy_table(p, dst, dst_entries)
 
 
 def fa_decode_paged(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, d, page_size,
@@ -322,6 +377,84 @@ def backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bo
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv, delta
+
+
+class Pager:
+    """Host page allocator of a paged KV cache (wraps ``fa_pager_*``): 16-token
+    pages handed to sequences from a free list, a page table [max_seqs,
+    max_pages] (-1 unused) to copy to the device."""
+
+    def __init__(self, num_pages: int, max_seqs: int, max_pages_per_seq: int):
+        self._p = fa_pager_create(num_pages, max_seqs, max_pages_per_seq)
+        if not self._p:
+            raise ValueError("fa_pager_create failed (sizes)")
+        self.num_pages, self.max_seqs, self.max_pages = num_pages, max_seqs, max_pages_per_seq
+
+    def close(self):
+        if self._p:
+            fa_pager_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reserve(self, seq: int, length: int) -> None:
+        st = fa_pager_reserve(self._p, seq, length)
+        if st != FA_OK:
+            raise FAError(st, "fa_pager_reserve")
+
+    def release(self, seq: int) -> None:
+        st = fa_pager_release(self._p, seq)
+        if st != FA_OK:
+            raise FAError(st, "fa_pager_release")
+
+    def length(self, seq: int) -> int:
+        return fa_pager_length(self._p, seq)
+
+    def free_pages(self) -> int:
+        return fa_pager_free_pages(self._p)
+
+    def table(self):
+        import numpy as np
+
+        out = np.empty((self.max_seqs, self.max_pages), dtype=np.int32)
+        st = fa_pager_copy_table(self._p, out.ctypes.data, out.size)
+        if st != FA_OK:
+            raise FAError(st, "fa_pager_copy_table")
+        return out
+
+
+def kv_append(k_new, v_new, seq_ids, positions, k_pages, v_pages, page_table, *, stream=None):
+    """Write new tokens' K/V rows [T, H_kv, d] into the pools [num_pages, H_kv,
+    16, d] at page_table[seq][pos // 16], row pos % 16 (int32 GPU tensors
+    seq_ids [T], positions [T], page_table [S, max_pages])."""
+    torch = _torch()
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("seq_ids", seq_ids),
+                    ("positions", positions), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("page_table", page_table)):
+        _check_dev(name, t)
+    T, Hkv, d = k_new.shape
+    num_pages, Hp, page_size, dp = k_pages.shape
+    if v_new.shape != k_new.shape or v_pages.shape != k_pages.shape or (Hp, dp) != (Hkv, d):
+        raise ValueError("k_new/v_new [T, H_kv, d] and pools [num_pages, H_kv, 16, d] must match")
+    for name, t in (("seq_ids", seq_ids), ("positions", positions)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (T,):
+            raise ValueError(f"{name} must be int32 [T]")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2:
+        raise ValueError("page_table must be int32 [S, max_pages]")
+    dt = _dtype_code(k_new)
+    if v_new.dtype != k_new.dtype or k_pages.dtype != k_new.dtype or v_pages.dtype != k_new.dtype:
+        raise TypeError("new rows and pools must share one dtype")
+    S, max_pages = page_table.shape
+    st = fa_kv_append(k_new.data_ptr(), v_new.data_ptr(), seq_ids.data_ptr(),
+                      positions.data_ptr(), T, k_pages.data_ptr(), v_pages.data_ptr(),
+                      page_table.data_ptr(), S, Hkv, d, page_size, max_pages, num_pages, dt,
+                      _stream_handle(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_kv_append")
 
 
 def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[float] = None,

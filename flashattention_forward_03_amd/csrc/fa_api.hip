@@ -58,6 +58,7 @@ const char *fa_status_str(int status)
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0; causal 0 or 1)";
+    case FA_ERR_NOMEM: return "not enough free pages";
     default: return "unknown status";
     }
 }
@@ -171,6 +172,33 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const vo
     const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "fa_bwd launch");
+    return FA_OK;
+}
+
+int fa_kv_append(const void *k_new, const void *v_new, const int32_t *seq_ids, const int32_t *positions, int T,
+                 void *k_pages, void *v_pages, const int32_t *page_table, int S, int H_kv, int d, int page_size,
+                 int max_pages_per_seq, int num_pages, int dtype, void *stream)
+{
+    if (T < 0 || S < 0 || H_kv < 1 || max_pages_per_seq < 1 || num_pages < 1)
+        return FA_ERR_SHAPE;
+    if (d < 8 || d > 256 || d % 8 != 0 || page_size != 16)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if ((long long)max_pages_per_seq * page_size > INT_MAX || (long long)S * max_pages_per_seq > INT_MAX)
+        return FA_ERR_SHAPE;
+    if (T == 0 || S == 0)
+        return FA_OK;
+    if (!k_new || !v_new || !seq_ids || !positions || !k_pages || !v_pages || !page_table)
+        return FA_ERR_NULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+        !aligned(seq_ids, 4) || !aligned(positions, 4) || !aligned(page_table, 4))
+        return FA_ERR_ALIGN;
+    fa::KvAppendArgs a{k_new, v_new, seq_ids, positions, T, k_pages, v_pages, page_table, S, H_kv, d,
+                       max_pages_per_seq, num_pages};
+    const hipError_t e = fa::launch_kv_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_kv_append launch");
     return FA_OK;
 }
 

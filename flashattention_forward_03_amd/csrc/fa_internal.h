@@ -60,6 +60,17 @@ struct BwdArgs {
 long long bwd_grid_size(int B, int H, int Nq, int Nk);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
+// Paged KV cache append: T new tokens' K/V rows [T, Hkv, d] into the pools.
+struct KvAppendArgs {
+    const void *k_new, *v_new;
+    const int32_t *seq_ids, *positions;
+    int T;
+    void *k_pages, *v_pages;
+    const int32_t *page_table;
+    int S, Hkv, d, max_pages, num_pages;
+};
+hipError_t launch_kv_append(const KvAppendArgs &a, hipStream_t stream);
+
 // Decode: cached tokens per split-KV chunk, and the launch.
 constexpr int kDecodeChunkPages = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }

@@ -3,7 +3,8 @@
  *
  * Two operations, both asynchronous on the caller's HIP stream (each also with
  * grouped-query heads, the _gqa calls; the forward also with strides and a
- * 16-bit O, fa_fwd_ex), and the forward's backward (fa_bwd):
+ * 16-bit O, fa_fwd_ex), the forward's backward (fa_bwd), and the paged cache's
+ * append kernel and host page allocator (fa_kv_append, fa_pager_*):
  *
  *   fa_fwd           exact attention forward: O = softmax(scale * Q K^T + mask) V
  *                    and the per-row log-sum-exp, computed tile by tile with an
@@ -29,8 +30,9 @@
  * stream go to the launch, no host round trip, no private allocation, error
  * read back right after the launch; and its design note that the op has no
  * CPU kernel):
- *   - Every pointer is a DEVICE pointer owned by the caller.  The library
- *     never allocates, frees, copies to/from the host or synchronises.
+ *   - Every pointer is a DEVICE pointer owned by the caller (except the
+ *     host-side page allocator, fa_pager_*).  The kernels' entry points never
+ *     allocate, free, copy to/from the host or synchronise.
  *   - `stream` is a hipStream_t passed as void*; NULL = the null stream.
  *   - Calls return once the kernels are enqueued.  Faults inside a kernel
  *     surface at the caller's next synchronisation.
@@ -64,6 +66,7 @@ extern "C" {
 #define FA_ERR_WORKSPACE 5   /* workspace missing or smaller than fa_decode_workspace_bytes */
 #define FA_ERR_HIP 6         /* a HIP launch failed; see fa_last_hip_error() */
 #define FA_ERR_ARG 7         /* scale not finite and > 0, or causal not 0/1 */
+#define FA_ERR_NOMEM 8       /* the page allocator has too few free pages */
 
 /* element types of Q, K, V (and the KV pools); FA_DTYPE_F32 only for fa_fwd_ex's O */
 #define FA_DTYPE_F16 0
@@ -223,6 +226,61 @@ int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages,
                         int S, int H, int H_kv, int d, int page_size, int max_pages_per_seq,
                         int num_pages, float scale, int dtype, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * Paged KV cache: append (inference kernel cookbook page, recipe 02 "KV Cache":
+ * store each token's K and V once for every later decode step; recipe 03: in
+ * fixed-size pages found through a page table).  Writes the K and V rows of
+ * T new tokens -- a prefill chunk or one token per sequence at a decode step --
+ * into the pools that fa_decode_paged reads:
+ *
+ *   k_new, v_new  [T, H_kv, d] f16/bf16, contiguous; 16-byte aligned
+ *   seq_ids       device int32 [T]: the sequence of each token, in [0, S)
+ *   positions     device int32 [T]: its logical position t in that sequence; the
+ *                 rows go to page page_table[s][t / 16], row t % 16
+ *   k_pages,
+ *   v_pages       [num_pages, H_kv, page_size, d] pools (written); 16-byte aligned
+ *   page_table    device int32 [S, max_pages_per_seq]
+ *   d             a multiple of 8 from 8 to 256;  page_size 16
+ *
+ * A token whose seq id, position or page entry is out of range is skipped (no
+ * write).  Two tokens with the same (sequence, position) in one call race.
+ * T or S of 0 is an empty call.
+ */
+int fa_kv_append(const void *k_new, const void *v_new, const int32_t *seq_ids,
+                 const int32_t *positions, int T, void *k_pages, void *v_pages,
+                 const int32_t *page_table, int S, int H_kv, int d, int page_size,
+                 int max_pages_per_seq, int num_pages, int dtype, void *stream);
+
+/*
+ * Paged KV cache: host-side page allocator (inference kernel cookbook page,
+ * recipe 03: pages instead of one contiguous buffer per sequence; NanoInfer
+ * page, paged KV-cache allocator).  Owns a host page table [max_seqs,
+ * max_pages_per_seq] (-1 where unused) and a free list of the pool's pages
+ * (a stack: the most recently freed page is reused first).  Pages are 16
+ * tokens.  This object lives in HOST memory allocated by the library; it
+ * touches no device memory: copy the table to the device array the kernels
+ * read.  Calls on one pager are serialised internally.
+ *
+ *   fa_pager_create    NULL for sizes < 1 or too large, or host allocation failure
+ *   fa_pager_reserve   grow sequence seq to hold len tokens (pages appended from
+ *                      the free list; never shrinks).  FA_ERR_NOMEM when the free
+ *                      list is too short (nothing changes), FA_ERR_SHAPE for a bad
+ *                      seq or len > max_pages_per_seq * 16
+ *   fa_pager_release   all pages of seq back to the free list; its length is 0
+ *   fa_pager_length    tokens reserved for seq (-1 for a bad pager or seq)
+ *   fa_pager_free_pages  pages on the free list (-1 for a NULL pager)
+ *   fa_pager_copy_table  copy the table (max_seqs * max_pages_per_seq int32)
+ *                      into dst; FA_ERR_SHAPE if dst_entries is smaller
+ */
+typedef struct fa_pager fa_pager;
+fa_pager *fa_pager_create(int num_pages, int max_seqs, int max_pages_per_seq);
+void fa_pager_destroy(fa_pager *p);
+int fa_pager_reserve(fa_pager *p, int seq, int len);
+int fa_pager_release(fa_pager *p, int seq);
+int fa_pager_length(const fa_pager *p, int seq);
+int fa_pager_free_pages(const fa_pager *p);
+int fa_pager_copy_table(const fa_pager *p, int32_t *dst, size_t dst_entries);
 
 /* Workspace bytes fa_decode_paged needs for these sizes (0 for invalid sizes). */
 size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size);

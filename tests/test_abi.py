@@ -272,3 +272,30 @@ def call_bwd(**over):
 ])
 def test_bwd_argument_checks(lib, over, status):
     assert call_bwd(**over) == status
+
+
+def call_append(**over):
+    a = dict(kn=A, vn=A, sid=A, pos=A, T=4, kp=A, vp=A, pt=A, S=2, H_kv=2, d=128, page_size=16,
+             max_pages=8, num_pages=64, dtype=1, stream=None)
+    a.update(over)
+    return fa.fa_kv_append(a["kn"], a["vn"], a["sid"], a["pos"], a["T"], a["kp"], a["vp"], a["pt"],
+                           a["S"], a["H_kv"], a["d"], a["page_size"], a["max_pages"],
+                           a["num_pages"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), fa.FA_ERR_SHAPE),
+    (dict(H_kv=0), fa.FA_ERR_SHAPE),
+    (dict(num_pages=0), fa.FA_ERR_SHAPE),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=264), fa.FA_ERR_UNSUPPORTED),
+    (dict(page_size=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(max_pages=1 << 28), fa.FA_ERR_SHAPE),
+    (dict(pos=None), fa.FA_ERR_NULL),
+    (dict(kp=A + 8), fa.FA_ERR_ALIGN),
+    (dict(sid=A + 2), fa.FA_ERR_ALIGN),
+    (dict(T=0, kn=None, vn=None, sid=None, pos=None), fa.FA_OK),
+])
+def test_kv_append_argument_checks(lib, over, status):
+    assert call_append(**over) == status

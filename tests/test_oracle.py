@@ -549,3 +549,42 @@ def test_backward_group_subset_equals_full():
     assert np.array_equal(part[0][1, 2:], full[0][1, 2:])
     assert np.array_equal(part[1][0, 0], full[1][0, 0]) and np.array_equal(part[2][1, 1], full[2][1, 1])
     assert np.isnan(part[1][0, 1]).all()
+
+
+# ------------------------------------------------------- paged cache append ---
+
+def test_kv_append_then_gather_is_the_logical_cache():
+    """Prefill in chunks, then one decode token per sequence: reading every
+    sequence back through its page table gives its tokens in order."""
+    from oracle import cache
+
+    inp = gen.decode_inputs(3, 4, 8, (1, 45), "bf16", 130, page_size=16, num_pages=32, Hkv=2)
+    kp = np.zeros((32, 2, 16, 8), np.uint16)
+    vp = np.zeros_like(kp)
+    # prefill each sequence in two chunks, interleaved across sequences
+    chunks = []
+    for s in range(inp.S):
+        a, b = int(inp.seq_off[s]), int(inp.seq_off[s + 1])
+        mid = a + (b - a) // 2
+        chunks += [(s, a, mid), (s, mid, b)]
+    for s, a, b in sorted(chunks, key=lambda c: c[1] - c[0]):
+        base = int(inp.seq_off[s])
+        n = cache.kv_append(kp, vp, inp.page_table, np.full(b - a, s), np.arange(a, b) - base,
+                            inp.k[a:b], inp.v[a:b])
+        assert n == b - a
+    assert np.array_equal(gen.gather_logical(kp, inp), inp.k)
+    assert np.array_equal(gen.gather_logical(vp, inp), inp.v)
+
+
+def test_kv_append_skips_out_of_range_tokens():
+    from oracle import cache
+
+    kp = np.zeros((4, 1, 16, 8), np.uint16)
+    vp = np.zeros_like(kp)
+    table = np.array([[2, -1], [7, 1]], np.int32)   # page 7 does not exist
+    new = np.arange(5 * 8, dtype=np.uint16).reshape(5, 1, 8) + 1
+    n = cache.kv_append(kp, vp, table, np.array([0, 0, 1, 2, 1]), np.array([3, 16, 0, 0, 20]),
+                        new, new)
+    assert n == 2                       # (0, 3) -> page 2; (1, 20) -> page 1 row 4
+    assert np.array_equal(kp[2, 0, 3], new[0, 0]) and np.array_equal(kp[1, 0, 4], new[4, 0])
+    assert int(np.count_nonzero(kp)) == 16
