@@ -52,8 +52,9 @@ template <bool BF16>
 constexpr float kRescaleLog2 = BF16 ? 32.0f : 15.0f;
 // Per-lane online-softmax state.
 struct RowState {
-    float m;   // running max, raw score units (-inf until a key is seen)
-    float l;   // running sum of exp2(s*c - m*c), fp32
+    float m;    // running max, raw score units (-inf until a key is seen)
+    float l;    // running sum of exp2(s*c - m*c), fp32
+    float mc;   // m*c, or 0 while m is -inf (kept, not recomputed per tile)
 };
 
 // Probabilities of one tile against the row's current (possibly stale) max
@@ -62,7 +63,7 @@ struct RowState {
 template <int NB, bool BF16>
 __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, float c_log2, u32x4_t (&pf)[2 * NB])
 {
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
@@ -73,7 +74,8 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
                 const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
                 const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
                 pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
-                ps[q] += p0 + p1;
+                // the first pair starts each partial sum (no 0 + x: x may be -0)
+                ps[q] = (blk == 0 && h2 == 0) ? p0 + p1 : ps[q] + (p0 + p1);
             }
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
@@ -88,13 +90,15 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
 // the exact path: tile max, new m = max(m, tile max), rescale of l and O by
 // alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
 // uniform) when O must be multiplied by alpha (done by the caller).
+// (Taking the exact path unconditionally on the first tile instead, so that
+// the check is one compare, measured slower: the extra branch costs spills.)
 template <int D, bool BF16>
 __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
                                              u32x4_t (&pf)[kBN<D> / 16], float c_log2, float tau_log2,
                                              float &alpha)
 {
     const float limit = exp2f(tau_log2);
-    float mc = st.m == -INFINITY ? 0.f : st.m * c_log2;
+    float mc = st.mc;
     alpha = 1.f;
     bool rescale = false;
     // at most two passes: the second one runs against the exact max (p <= 1)
@@ -118,6 +122,7 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
         alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
         st.m = m_new;
         mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
+        st.mc = mc;
         rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
     }
     return rescale;
@@ -188,7 +193,7 @@ __device__ __forceinline__ void attend_qtile(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    RowState st{-INFINITY, 0.f};
+    RowState st{-INFINITY, 0.f, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
     const u32x4s_t krsrc = make_rsrc(Kb, Nk * krs), vrsrc = make_rsrc(Vb, Nk * vrs);
