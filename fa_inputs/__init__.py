@@ -21,10 +21,14 @@ Recipe (every workload):
     (``[sum(kv_len), Hkv, d]``), then the page placement: a seeded permutation
     of the page pool; sequence s's p-th logical page goes to
     ``perm[sum_{s'<s} ceil(kv_len[s']/page) + p]``.
+  * Pre-LayerNorm block draw order (``block_inputs``): per-row offsets and
+    scales, the activations, LayerNorm gamma and beta, the Q/K/V weights and
+    biases, the output weights and bias (recipe in its docstring).
 
 The workloads are the attention shapes of the pages (the forward at N=2048,
 d=64 of the flash-attention recipe, a causal B8 H16 d64 sweep, an encoder
-shape with per-sequence key padding, and decode over a paged cache).
+shape with per-sequence key padding, decode over a paged cache, and the
+encoder block of the BERT-large runs: hidden 1024 = 16 heads x 64).
 """
 from __future__ import annotations
 
@@ -253,6 +257,82 @@ def gather_logical(pool: np.ndarray, inp: DecodeInputs) -> np.ndarray:
     return pool[phys, :, row, :]
 
 
+# ------------------------------------------------------ pre-LN block ---
+
+@dataclasses.dataclass
+class BlockInputs:
+    """One pre-LayerNorm attention block: activations, LayerNorm parameters and
+    the two dense layers (weights output-major, as a dense layer's matrix)."""
+    x: np.ndarray            # uint16 [B*N, C]   (token t = b*N + n), C = H*d
+    gamma: np.ndarray        # float32 [C]
+    beta: np.ndarray         # float32 [C]
+    w_qkv: np.ndarray        # uint16 [(H + 2*Hkv)*d, C]  rows: Q heads, K heads, V heads
+    b_qkv: np.ndarray        # float32 [(H + 2*Hkv)*d]
+    w_o: np.ndarray          # uint16 [C, H*d]
+    b_o: np.ndarray          # float32 [C]
+    B: int
+    N: int
+    H: int
+    Hkv: int
+    d: int
+    dtype: str
+    eps: float
+    scale: float
+    causal: bool
+    kv_lens: Optional[np.ndarray]   # int32 [B] or None
+    seed: int
+
+    @property
+    def C(self):
+        return self.H * self.d
+
+    @property
+    def T(self):
+        return self.B * self.N
+
+
+def block_inputs(B: int, N: int, H: int, d: int, dtype: str, seed: int, *,
+                 Hkv: Optional[int] = None, causal: bool = False, eps: float = 1e-5,
+                 scale: Optional[float] = None, row_offset: float = 1.0,
+                 kv_len_range: Optional[tuple] = None) -> BlockInputs:
+    """Draw one block's inputs.
+
+    Draw order: per-row offsets ``uniform(-row_offset, row_offset)`` [T] and
+    scales ``uniform(0.5, 2)`` [T], z ~ N(0, 1) [T, C] (x = offset + scale * z,
+    a residual stream whose rows differ in mean and spread), gamma = 1 +
+    0.1 N(0, 1), beta = 0.1 N(0, 1), W_qkv = N(0, 1) / sqrt(C), b_qkv =
+    0.02 N(0, 1), W_o = N(0, 1) / sqrt(H*d), b_o = 0.02 N(0, 1), then the
+    key lengths when a padding range is given.  Weights and x are rounded to
+    the 16-bit dtype; gamma, beta and the biases stay float32.
+    """
+    Hkv = H if Hkv is None else Hkv
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    T, C = B * N, H * d
+    R = (H + 2 * Hkv) * d
+    rng = np.random.default_rng(seed)
+    off = rng.uniform(-row_offset, row_offset, size=T).astype(np.float32)
+    scl = rng.uniform(0.5, 2.0, size=T).astype(np.float32)
+    z = rng.standard_normal((T, C), dtype=np.float32)
+    x = round_bits(off[:, None] + scl[:, None] * z, dtype)
+    gamma = (1.0 + 0.1 * rng.standard_normal(C, dtype=np.float32)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(C, dtype=np.float32)).astype(np.float32)
+    w_qkv = round_bits(rng.standard_normal((R, C), dtype=np.float32) / np.float32(math.sqrt(C)),
+                       dtype)
+    b_qkv = (0.02 * rng.standard_normal(R, dtype=np.float32)).astype(np.float32)
+    w_o = round_bits(rng.standard_normal((C, H * d), dtype=np.float32)
+                     / np.float32(math.sqrt(H * d)), dtype)
+    b_o = (0.02 * rng.standard_normal(C, dtype=np.float32)).astype(np.float32)
+    kv_lens = None
+    if kv_len_range is not None:
+        lo, hi = kv_len_range
+        kv_lens = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return BlockInputs(x, gamma, beta, w_qkv, b_qkv, w_o, b_o, B, N, H, Hkv, d, dtype,
+                       float(eps), float(scale), bool(causal), kv_lens, seed)
+
+
 # -------------------------------------------------------------- workloads ---
 
 # Named workloads: the forward shapes and the decode batch the measurements
@@ -282,6 +362,13 @@ FWD_WORKLOADS = {
                                                seed=3004),
 }
 
+# The encoder block of the pages' BERT-large runs (hidden 1024 = 16 heads x 64),
+# at the attention workload's batch and length, non-causal as an encoder is.
+BLOCK_WORKLOADS = {
+    "prenorm_block_b8_n4096_h16_d64_bf16": dict(B=8, N=4096, H=16, d=64, dtype="bf16",
+                                                causal=False, seed=6000),
+}
+
 DECODE_WORKLOADS = {
     "decode_paged_s32h32_d128_bf16": dict(S=32, H=32, d=128, len_range=(512, 8192),
                                           dtype="bf16", page_size=16, num_pages=1 << 16,
@@ -307,3 +394,11 @@ def decode_workload(name: str, **over) -> DecodeInputs:
     S, H, d = w.pop("S"), w.pop("H"), w.pop("d")
     len_range, dtype, seed = w.pop("len_range"), w.pop("dtype"), w.pop("seed")
     return decode_inputs(S, H, d, len_range, dtype, seed, **w)
+
+
+def block_workload(name: str, **over) -> BlockInputs:
+    w = dict(BLOCK_WORKLOADS[name])
+    w.update(over)
+    B, N, H, d = w.pop("B"), w.pop("N"), w.pop("H"), w.pop("d")
+    dtype, seed = w.pop("dtype"), w.pop("seed")
+    return block_inputs(B, N, H, d, dtype, seed, **w)
