@@ -46,7 +46,9 @@ FA_DTYPE_F32 = 2
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_bwd", "fa_decode_paged", "fa_decode_paged_gqa",
             "fa_kv_append", "fa_pager_create", "fa_pager_destroy", "fa_pager_reserve",
             "fa_pager_release", "fa_pager_length", "fa_pager_free_pages", "fa_pager_copy_table",
-            "fa_decode_workspace_bytes", "fa_status_str", "fa_last_hip_error", "fa_version")
+            "fa_decode_workspace_bytes", "fa_ln_stats", "fa_ln_fold_weights", "fa_ln_linear",
+            "fa_linear", "fa_prenorm_attention_workspace_bytes", "fa_prenorm_attention",
+            "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -121,6 +123,19 @@ def load_library():
     lib.fa_decode_paged_gqa.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_decode_workspace_bytes.restype = Z
+    lib.fa_ln_stats.argtypes = [P, P, P, I, I, F, I, P]
+    lib.fa_ln_stats.restype = I
+    lib.fa_ln_fold_weights.argtypes = [P, P, P, P, P, P, P, I, I, I, P]
+    lib.fa_ln_fold_weights.restype = I
+    lib.fa_ln_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P]
+    lib.fa_ln_linear.restype = I
+    lib.fa_linear.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    lib.fa_linear.restype = I
+    lib.fa_prenorm_attention_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_prenorm_attention_workspace_bytes.restype = Z
+    lib.fa_prenorm_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, F, I, P, I, P, Z,
+                                         P]
+    lib.fa_prenorm_attention.restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -219,6 +234,37 @@ def fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, 
 
 def fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size) -> int:
     return int(load_library().fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size))
+
+
+def fa_ln_stats(x, mean, rstd, T, C, eps, dtype, stream) -> int:
+    return load_library().fa_ln_stats(x, mean, rstd, T, C, eps, dtype, stream)
+
+
+def fa_ln_fold_weights(gamma, beta, w, bias, w_folded, bias_folded, colsum, N, C, dtype,
+                       stream) -> int:
+    return load_library().fa_ln_fold_weights(gamma, beta, w, bias, w_folded, bias_folded, colsum,
+                                             N, C, dtype, stream)
+
+
+def fa_ln_linear(x, mean, rstd, w_folded, bias_folded, colsum, y, T, C, N, dtype, stream) -> int:
+    return load_library().fa_ln_linear(x, mean, rstd, w_folded, bias_folded, colsum, y, T, C, N,
+                                       dtype, stream)
+
+
+def fa_linear(a, w, bias, residual, y, M, K, N, dtype, stream) -> int:
+    return load_library().fa_linear(a, w, bias, residual, y, M, K, N, dtype, stream)
+
+
+def fa_prenorm_attention_workspace_bytes(B, N, H, H_kv, d) -> int:
+    return load_library().fa_prenorm_attention_workspace_bytes(B, N, H, H_kv, d)
+
+
+def fa_prenorm_attention(x, w_qkv_folded, b_qkv_folded, colsum_qkv, w_o, b_o, y, B, N, H, H_kv, d,
+                         eps, scale, causal, kv_lens, dtype, workspace, workspace_bytes,
+                         stream) -> int:
+    return load_library().fa_prenorm_attention(x, w_qkv_folded, b_qkv_folded, colsum_qkv, w_o, b_o,
+                                               y, B, N, H, H_kv, d, eps, scale, causal, kv_lens,
+                                               dtype, workspace, workspace_bytes, stream)
 
 
 def fa_status_str(status: int) -> str:
@@ -505,3 +551,165 @@ def decode_paged(q, k_pages, v_pages, page_table, kv_lens, *, scale: Optional[fl
     if st != FA_OK:
         raise FAError(st, "fa_decode_paged" if Hkv == H else "fa_decode_paged_gqa")
     return o, lse
+
+
+# ------------------------------------------------------ pre-LN block wrappers
+
+def _f32_vec(name, t, n):
+    torch = _torch()
+    _check_dev(name, t)
+    if t.dtype != torch.float32 or tuple(t.shape) != (n,):
+        raise ValueError(f"{name} must be float32 [{n}]")
+    return t.data_ptr()
+
+
+def _mat16(name, t, shape):
+    _check_dev(name, t)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    return t.data_ptr()
+
+
+def _call(name, st):
+    if st != FA_OK:
+        raise FAError(st, name)
+
+
+def ln_stats(x, eps: float = 1e-5, *, stream=None):
+    """Per-row mean and 1/sqrt(var + eps) (fp32 [T]) of x [T, C] f16/bf16."""
+    torch = _torch()
+    T, C = x.shape
+    dt = _dtype_code(x)
+    _mat16("x", x, (T, C))
+    mean = torch.empty(T, dtype=torch.float32, device=x.device)
+    rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _call("fa_ln_stats", fa_ln_stats(x.data_ptr(), mean.data_ptr(), rstd.data_ptr(), T, C,
+                                     float(eps), dt, _stream_handle(stream)))
+    return mean, rstd
+
+
+def ln_fold_weights(gamma, beta, w, bias=None, *, stream=None):
+    """Fold LayerNorm's gamma and beta into a dense layer w [N, C]: returns
+    (w_folded [N, C] in w's dtype, bias_folded fp32 [N], colsum fp32 [N])."""
+    torch = _torch()
+    N, C = w.shape
+    dt = _dtype_code(w)
+    _mat16("w", w, (N, C))
+    g = _f32_vec("gamma", gamma, C)
+    b = _f32_vec("beta", beta, C)
+    bp = None if bias is None else _f32_vec("bias", bias, N)
+    wf = torch.empty_like(w)
+    bf = torch.empty(N, dtype=torch.float32, device=w.device)
+    cs = torch.empty(N, dtype=torch.float32, device=w.device)
+    _call("fa_ln_fold_weights", fa_ln_fold_weights(g, b, w.data_ptr(), bp, wf.data_ptr(),
+                                                   bf.data_ptr(), cs.data_ptr(), N, C, dt,
+                                                   _stream_handle(stream)))
+    return wf, bf, cs
+
+
+def ln_linear(x, mean, rstd, folded, *, stream=None, out=None):
+    """LayerNorm(x) w^T + bias for x [T, C] from ``ln_stats`` and the
+    ``ln_fold_weights`` triple; returns y [T, N] in x's dtype."""
+    torch = _torch()
+    wf, bf, cs = folded
+    T, C = x.shape
+    N = wf.shape[0]
+    dt = _dtype_code(x)
+    if wf.dtype != x.dtype:
+        raise TypeError("x and the folded weights must share one dtype")
+    _mat16("x", x, (T, C))
+    _mat16("w_folded", wf, (N, C))
+    y = torch.empty((T, N), dtype=x.dtype, device=x.device) if out is None else out
+    _mat16("y", y, (T, N))
+    _call("fa_ln_linear", fa_ln_linear(x.data_ptr(), _f32_vec("mean", mean, T),
+                                       _f32_vec("rstd", rstd, T), wf.data_ptr(),
+                                       _f32_vec("bias_folded", bf, N), _f32_vec("colsum", cs, N),
+                                       y.data_ptr(), T, C, N, dt, _stream_handle(stream)))
+    return y
+
+
+def linear(a, w, bias=None, residual=None, *, stream=None, out=None):
+    """a [M, K] w [N, K]^T + bias (+ residual [M, N]); returns y [M, N] in a's dtype."""
+    torch = _torch()
+    M, K = a.shape
+    N = w.shape[0]
+    dt = _dtype_code(a)
+    if w.dtype != a.dtype or (residual is not None and residual.dtype != a.dtype):
+        raise TypeError("a, w and residual must share one dtype")
+    _mat16("a", a, (M, K))
+    _mat16("w", w, (N, K))
+    rp = None if residual is None else _mat16("residual", residual, (M, N))
+    bp = None if bias is None else _f32_vec("bias", bias, N)
+    y = torch.empty((M, N), dtype=a.dtype, device=a.device) if out is None else out
+    _mat16("y", y, (M, N))
+    _call("fa_linear", fa_linear(a.data_ptr(), w.data_ptr(), bp, rp, y.data_ptr(), M, K, N, dt,
+                                 _stream_handle(stream)))
+    return y
+
+
+def prenorm_attention(x, qkv_folded, w_o, b_o, *, B: int, N: int, H: int, H_kv: Optional[int] = None,
+                      eps: float = 1e-5, scale: Optional[float] = None, causal: bool = False,
+                      kv_lens=None, workspace=None, stream=None, out=None):
+    """The pre-LayerNorm attention block y = x + Attn(LN(x) W_qkv^T + b_qkv) W_o^T + b_o.
+
+    x [B*N, C] f16/bf16 (C = H*d); ``qkv_folded`` = ``ln_fold_weights(gamma,
+    beta, W_qkv, b_qkv)`` with W_qkv [(H + 2*H_kv)*d, C] (query heads, key
+    heads, value heads); w_o [C, C]; b_o fp32 [C] or None.  ``workspace``: a
+    uint8 GPU tensor of at least ``fa_prenorm_attention_workspace_bytes``
+    bytes (allocated when None).  Returns (y, workspace)."""
+    torch = _torch()
+    H_kv = H if H_kv is None else H_kv
+    T, C = x.shape
+    if T != B * N or C % H:
+        raise ValueError("x must be [B*N, H*d]")
+    d = C // H
+    wf, bf, cs = qkv_folded
+    R = (H + 2 * H_kv) * d
+    dt = _dtype_code(x)
+    if wf.dtype != x.dtype or w_o.dtype != x.dtype:
+        raise TypeError("x and the weights must share one dtype")
+    _mat16("x", x, (T, C))
+    _mat16("w_qkv_folded", wf, (R, C))
+    _mat16("w_o", w_o, (C, C))
+    bo = None if b_o is None else _f32_vec("b_o", b_o, C)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl_ptr = None
+    if kv_lens is not None:
+        _check_dev("kv_lens", kv_lens)
+        if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+            raise ValueError("kv_lens must be int32 [B]")
+        kl_ptr = kv_lens.data_ptr()
+    need = fa_prenorm_attention_workspace_bytes(B, N, H, H_kv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check_dev("workspace", workspace)
+    y = torch.empty_like(x) if out is None else out
+    _mat16("y", y, (T, C))
+    _call("fa_prenorm_attention",
+          fa_prenorm_attention(x.data_ptr(), wf.data_ptr(), _f32_vec("b_qkv_folded", bf, R),
+                               _f32_vec("colsum_qkv", cs, R), w_o.data_ptr(), bo, y.data_ptr(), B,
+                               N, H, H_kv, d, float(eps), float(scale), int(bool(causal)), kl_ptr,
+                               dt, workspace.data_ptr(), workspace.numel(),
+                               _stream_handle(stream)))
+    return y, workspace
+
+
+def prenorm_workspace_views(workspace, B: int, N: int, H: int, H_kv: int, d: int, dtype):
+    """Views of the block's stages inside its workspace, in the documented order
+    (mean, rstd, qkv, o, lse; each on a 256-byte boundary)."""
+    torch = _torch()
+    up = lambda v: (v + 255) // 256 * 256
+    T, C, R = B * N, H * d, (H + 2 * H_kv) * d
+    offs = {}
+    o = 0
+    for name, nbytes in (("mean", T * 4), ("rstd", T * 4), ("qkv", T * R * 2), ("o", T * C * 2),
+                         ("lse", B * H * N * 4)):
+        offs[name] = (o, nbytes)
+        o += up(nbytes)
+    def view(name, dt, shape):
+        a, n = offs[name]
+        return workspace[a:a + n].view(dt).view(*shape)
+    return dict(mean=view("mean", torch.float32, (T,)), rstd=view("rstd", torch.float32, (T,)),
+                qkv=view("qkv", dtype, (T, R)), o=view("o", dtype, (T, C)),
+                lse=view("lse", torch.float32, (B, H, N)))

@@ -32,6 +32,43 @@ int hip_fail(hipError_t e, const char *what)
 }
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+bool eps_ok(float e) { return std::isfinite(e) && e >= 0.f; }
+
+// Dense-layer GEMM sizes: M rows, K inputs (a multiple of 64, 16-byte
+// copies of 64-element k-steps, 32-bit offsets over 256 rows), N outputs (a
+// multiple of 8: 4-element stores and 16-byte bias reads).
+int gemm_check(int M, int K, int N, int dtype)
+{
+    if (M < 0 || K < 0 || N < 0)
+        return FA_ERR_SHAPE;
+    if (K < 64 || K % 64 != 0 || N % 8 != 0)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if ((long long)K * 512 >= (1LL << 31) || fa::gemm_grid_size(M, N) > INT_MAX)
+        return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+// Byte offsets of the block's stages in its workspace (256-byte aligned).
+struct BlockLayout {
+    size_t mean, rstd, qkv, o, lse, total;
+};
+
+bool block_layout(int B, int N, int H, int H_kv, int d, BlockLayout &L)
+{
+    if (B < 0 || N < 0 || H < 0 || d < 0 || (H > 0 && (H_kv < 1 || H % H_kv != 0)))
+        return false;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t T = (size_t)B * N, C = (size_t)H * d, R = ((size_t)H + 2 * (size_t)H_kv) * d;
+    L.mean = 0;
+    L.rstd = L.mean + up(T * 4);
+    L.qkv = L.rstd + up(T * 4);
+    L.o = L.qkv + up(T * R * 2);
+    L.lse = L.o + up(T * C * 2);
+    L.total = L.lse + up((size_t)B * H * N * 4);
+    return true;
+}
 
 size_t decode_ws_bytes(long long S, long long H, long long d, int max_pages)
 {
@@ -57,7 +94,7 @@ const char *fa_status_str(int status)
     case FA_ERR_ALIGN: return "pointer not aligned as required";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP launch failed";
-    case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0; causal 0 or 1)";
+    case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0; causal 0 or 1; eps finite and >= 0)";
     case FA_ERR_NOMEM: return "not enough free pages";
     default: return "unknown status";
     }
@@ -263,6 +300,166 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
 {
     return fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H, d, page_size,
                                max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------ pre-LN block ---
+
+int fa_ln_stats(const void *x, float *mean, float *rstd, int T, int C, float eps, int dtype, void *stream)
+{
+    if (T < 0 || C < 0)
+        return FA_ERR_SHAPE;
+    if (C < 8 || C % 8 != 0)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (!eps_ok(eps))
+        return FA_ERR_ARG;
+    if (T == 0)
+        return FA_OK;
+    if (!x || !mean || !rstd)
+        return FA_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(mean, 16) || !aligned(rstd, 16))
+        return FA_ERR_ALIGN;
+    const hipError_t e =
+        fa::launch_ln_stats(x, mean, rstd, T, C, eps, dtype == FA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_ln_stats launch");
+    return FA_OK;
+}
+
+int fa_ln_fold_weights(const float *gamma, const float *beta, const void *w, const float *bias, void *w_folded,
+                       float *bias_folded, float *colsum, int N, int C, int dtype, void *stream)
+{
+    if (N < 0 || C < 0)
+        return FA_ERR_SHAPE;
+    if (C < 8 || C % 8 != 0)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (N == 0)
+        return FA_OK;
+    if (!gamma || !beta || !w || !w_folded || !bias_folded || !colsum)
+        return FA_ERR_NULL;
+    if (!aligned(gamma, 16) || !aligned(beta, 16) || !aligned(w, 16) || !aligned(bias, 16) ||
+        !aligned(w_folded, 16) || !aligned(bias_folded, 16) || !aligned(colsum, 16))
+        return FA_ERR_ALIGN;
+    const hipError_t e = fa::launch_ln_fold(gamma, beta, w, bias, w_folded, bias_folded, colsum, N, C,
+                                            dtype == FA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_ln_fold_weights launch");
+    return FA_OK;
+}
+
+int fa_ln_linear(const void *x, const float *mean, const float *rstd, const void *w_folded, const float *bias_folded,
+                 const float *colsum, void *y, int T, int C, int N, int dtype, void *stream)
+{
+    const int st = gemm_check(T, C, N, dtype);
+    if (st != FA_OK || T == 0 || N == 0)
+        return st;
+    if (!x || !mean || !rstd || !w_folded || !bias_folded || !colsum || !y)
+        return FA_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(mean, 16) || !aligned(rstd, 16) || !aligned(w_folded, 16) ||
+        !aligned(bias_folded, 16) || !aligned(colsum, 16) || !aligned(y, 16))
+        return FA_ERR_ALIGN;
+    const fa::GemmArgs g{x, w_folded, y, T, N, C, mean, rstd, colsum, bias_folded, nullptr};
+    const hipError_t e =
+        fa::launch_gemm(g, fa::GEMM_EPI_LN, dtype == FA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_ln_linear launch");
+    return FA_OK;
+}
+
+int fa_linear(const void *a, const void *w, const float *bias, const void *residual, void *y, int M, int K, int N,
+              int dtype, void *stream)
+{
+    const int st = gemm_check(M, K, N, dtype);
+    if (st != FA_OK || M == 0 || N == 0)
+        return st;
+    if (!a || !w || !y)
+        return FA_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(bias, 16) || !aligned(residual, 16) || !aligned(y, 16))
+        return FA_ERR_ALIGN;
+    const fa::GemmArgs g{a, w, y, M, N, K, nullptr, nullptr, nullptr, bias, residual};
+    const hipError_t e =
+        fa::launch_gemm(g, fa::GEMM_EPI_BIAS, dtype == FA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_linear launch");
+    return FA_OK;
+}
+
+size_t fa_prenorm_attention_workspace_bytes(int B, int N, int H, int H_kv, int d)
+{
+    BlockLayout L;
+    if (!block_layout(B, N, H, H_kv, d, L))
+        return 0;
+    return L.total;
+}
+
+int fa_prenorm_attention(const void *x, const void *w_qkv_folded, const float *b_qkv_folded, const float *colsum_qkv,
+                         const void *w_o, const float *b_o, void *y, int B, int N, int H, int H_kv, int d,
+                         float eps, float scale, int causal, const int32_t *kv_lens, int dtype, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || N < 0 || H < 0)
+        return FA_ERR_SHAPE;
+    if (H > 0 && (H_kv < 1 || H % H_kv != 0))
+        return FA_ERR_SHAPE;
+    if (d < 8 || d > 128 || d % 8 != 0)
+        return FA_ERR_UNSUPPORTED;
+    const long long C = (long long)H * d, R = (long long)(H + 2 * (long long)H_kv) * d, T = (long long)B * N;
+    if (H > 0 && C % 64 != 0)
+        return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (!eps_ok(eps) || !scale_ok(scale) || (causal != 0 && causal != 1))
+        return FA_ERR_ARG;
+    if (T == 0 || H == 0)
+        return FA_OK;
+    // every stage's limits, before anything is launched
+    if (T > INT_MAX || C * 512 >= (1LL << 31) || R > INT_MAX || fa::gemm_grid_size((int)T, (int)R) > INT_MAX ||
+        fa::fwd_grid_size(B, H, N) > INT_MAX || ((long long)N + 64) * R * 2 > INT_MAX)
+        return FA_ERR_SHAPE;
+    BlockLayout L;
+    if (!block_layout(B, N, H, H_kv, d, L))
+        return FA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < L.total)
+        return FA_ERR_WORKSPACE;
+    if (!x || !w_qkv_folded || !b_qkv_folded || !colsum_qkv || !w_o || !y)
+        return FA_ERR_NULL;
+    if (!aligned(workspace, 256))
+        return FA_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(w_qkv_folded, 16) || !aligned(b_qkv_folded, 16) || !aligned(colsum_qkv, 16) ||
+        !aligned(w_o, 16) || !aligned(b_o, 16) || !aligned(y, 16) || !aligned(kv_lens, 4))
+        return FA_ERR_ALIGN;
+
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *mean = reinterpret_cast<float *>(ws + L.mean);
+    float *rstd = reinterpret_cast<float *>(ws + L.rstd);
+    uint16_t *qkv = reinterpret_cast<uint16_t *>(ws + L.qkv);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + L.o);
+    float *lse = reinterpret_cast<float *>(ws + L.lse);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == FA_DTYPE_BF16;
+
+    hipError_t e = fa::launch_ln_stats(x, mean, rstd, (int)T, (int)C, eps, bf16, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_prenorm_attention stats launch");
+    const fa::GemmArgs gq{x, w_qkv_folded, qkv, (int)T, (int)R, (int)C, mean, rstd, colsum_qkv, b_qkv_folded, nullptr};
+    e = fa::launch_gemm(gq, fa::GEMM_EPI_LN, bf16, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_prenorm_attention qkv launch");
+    // q, k, v are column ranges of the qkv rows: [b, n, head, d]
+    const int64_t qs[3] = {(int64_t)N * R, d, R};
+    const int64_t os[3] = {(int64_t)N * C, d, C};
+    const int st = fa_fwd_ex(qkv, qkv + (size_t)H * d, qkv + (size_t)(H + H_kv) * d, o, lse, B, H, H_kv, N, N, d, qs,
+                             qs, qs, os, scale, causal, kv_lens, dtype, dtype, stream);
+    if (st != FA_OK)
+        return st;
+    const fa::GemmArgs go{o, w_o, y, (int)T, (int)C, (int)C, nullptr, nullptr, nullptr, b_o, x};
+    e = fa::launch_gemm(go, fa::GEMM_EPI_BIAS, bf16, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "fa_prenorm_attention output launch");
+    return FA_OK;
 }
 
 }  // extern "C"

@@ -71,6 +71,26 @@ struct KvAppendArgs {
 };
 hipError_t launch_kv_append(const KvAppendArgs &a, hipStream_t stream);
 
+// Pre-LayerNorm block: row statistics, the LayerNorm fold of a dense layer's
+// weights, and the dense-layer GEMM Y[M, N] = A[M, K] W[N, K]^T (row-major,
+// 16-bit, contiguous) with the LayerNorm or the bias (+ residual) epilogue.
+constexpr int GEMM_EPI_LN = 0;     // y = rstd[t] (acc - mean[t] colsum[n]) + bias[n]
+constexpr int GEMM_EPI_BIAS = 1;   // y = acc + bias[n] (+ res[t, n])
+struct GemmArgs {
+    const void *a, *w;
+    void *y;
+    int M, N, K;                         // K a multiple of 64, N of 8
+    const float *mean, *rstd, *colsum;   // LN epilogue
+    const float *bias;                   // [N] or NULL
+    const void *res;                     // [M, N] or NULL (bias epilogue)
+};
+hipError_t launch_ln_stats(const void *x, float *mean, float *rstd, int T, int C, float eps, bool bf16,
+                           hipStream_t stream);
+hipError_t launch_ln_fold(const float *gamma, const float *beta, const void *w, const float *bias, void *w_folded,
+                          float *bias_folded, float *colsum, int N, int C, bool bf16, hipStream_t stream);
+long long gemm_grid_size(int M, int N);
+hipError_t launch_gemm(const GemmArgs &g, int epi, bool bf16, hipStream_t stream);
+
 // Decode: cached tokens per split-KV chunk, and the launch.
 constexpr int kDecodeChunkPages = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }

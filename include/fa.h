@@ -4,7 +4,9 @@
  * Two operations, both asynchronous on the caller's HIP stream (each also with
  * grouped-query heads, the _gqa calls; the forward also with strides and a
  * 16-bit O, fa_fwd_ex), the forward's backward (fa_bwd), and the paged cache's
- * append kernel and host page allocator (fa_kv_append, fa_pager_*):
+ * append kernel and host page allocator (fa_kv_append, fa_pager_*), and the
+ * pre-LayerNorm attention block around the forward (fa_ln_*, fa_linear,
+ * fa_prenorm_attention):
  *
  *   fa_fwd           exact attention forward: O = softmax(scale * Q K^T + mask) V
  *                    and the per-row log-sum-exp, computed tile by tile with an
@@ -65,7 +67,7 @@ extern "C" {
 #define FA_ERR_ALIGN 4       /* a pointer is not aligned as stated below */
 #define FA_ERR_WORKSPACE 5   /* workspace missing or smaller than fa_decode_workspace_bytes */
 #define FA_ERR_HIP 6         /* a HIP launch failed; see fa_last_hip_error() */
-#define FA_ERR_ARG 7         /* scale not finite and > 0, or causal not 0/1 */
+#define FA_ERR_ARG 7         /* scale not finite and > 0, causal not 0/1, or eps not finite and >= 0 */
 #define FA_ERR_NOMEM 8       /* the page allocator has too few free pages */
 
 /* element types of Q, K, V (and the KV pools); FA_DTYPE_F32 only for fa_fwd_ex's O */
@@ -281,6 +283,79 @@ int fa_pager_release(fa_pager *p, int seq);
 int fa_pager_length(const fa_pager *p, int seq);
 int fa_pager_free_pages(const fa_pager *p);
 int fa_pager_copy_table(const fa_pager *p, int32_t *dst, size_t dst_entries);
+
+/*
+ * Pre-LayerNorm attention block: the encoder layer of the
+ * Kernel-Inference-Engine page's charts (x -> LayerNorm -> dense Q/K/V ->
+ * softmax(QK^T/sqrt(d)) V -> dense W_O -> + x), with the LayerNorm folded into
+ * the Q/K/V projection so that no normalised activation is stored (the page's
+ * fused kernel folds it into the attention prologue; its LayerNorm kernel uses
+ * Welford's one-pass mean and variance).
+ *
+ * Matrices are row-major, contiguous, in the 16-bit dtype (FA_DTYPE_F16 or
+ * FA_DTYPE_BF16), 16-byte aligned; dense weights are output-major [N, K] (row
+ * n holds the K input weights of output n).  LayerNorm parameters, biases and
+ * statistics are fp32, 16-byte aligned.  LayerNorm(x) = (x - mean) / sqrt(var
+ * + eps) * gamma + beta with the row's population variance; eps must be finite
+ * and >= 0 (else FA_ERR_ARG).
+ *
+ *   fa_ln_stats         mean[t] and rstd[t] = 1/sqrt(var + eps) of the T rows of
+ *                       x [T, C] (C a multiple of 8).
+ *   fa_ln_fold_weights  once per weight set: w_folded[n, k] = gamma[k] w[n, k]
+ *                       rounded to the dtype, bias_folded[n] = bias[n] +
+ *                       sum_k beta[k] w[n, k] (bias may be NULL = 0), colsum[n] =
+ *                       sum_k w_folded[n, k].  w [N, C], C a multiple of 8.
+ *   fa_ln_linear        y = LayerNorm(x) w^T + bias for x [T, C], from the
+ *                       statistics and the folded weights: y[t, n] = rstd[t] *
+ *                       (sum_k x[t, k] w_folded[n, k] - mean[t] colsum[n]) +
+ *                       bias_folded[n], accumulated in fp32, rounded once to the
+ *                       dtype.  y [T, N]; C a multiple of 64, N of 8.
+ *   fa_linear           y = a w^T + bias (+ residual) for a [M, K], w [N, K],
+ *                       bias [N] (NULL = 0), residual [M, N] (NULL = none); fp32
+ *                       accumulation, one rounding.  K a multiple of 64, N of 8.
+ *
+ * Sizes: T, M of 0 is an empty call; negative sizes or K * 512 >= 2^31 are
+ * FA_ERR_SHAPE; a C, K or N that is not the stated multiple is
+ * FA_ERR_UNSUPPORTED.  Outputs must not overlap inputs.
+ */
+int fa_ln_stats(const void *x, float *mean, float *rstd, int T, int C, float eps, int dtype, void *stream);
+int fa_ln_fold_weights(const float *gamma, const float *beta, const void *w, const float *bias,
+                       void *w_folded, float *bias_folded, float *colsum, int N, int C, int dtype,
+                       void *stream);
+int fa_ln_linear(const void *x, const float *mean, const float *rstd, const void *w_folded,
+                 const float *bias_folded, const float *colsum, void *y, int T, int C, int N,
+                 int dtype, void *stream);
+int fa_linear(const void *a, const void *w, const float *bias, const void *residual, void *y, int M,
+              int K, int N, int dtype, void *stream);
+
+/*
+ * The whole block, y = x + Attention(LayerNorm(x) W_qkv^T + b_qkv) W_o^T + b_o,
+ * for x [B*N, C] (token t = b*N + n), C = H*d:
+ *
+ *   w_qkv_folded, b_qkv_folded, colsum_qkv
+ *                 fa_ln_fold_weights of W_qkv [(H + 2*H_kv)*d, C] (output rows:
+ *                 the H query heads, then the H_kv key heads, then the H_kv
+ *                 value heads, d each), b_qkv, gamma and beta
+ *   w_o, b_o      W_o [C, H*d], b_o [C] (NULL = 0)
+ *   y             [B*N, C] (must not overlap x)
+ *   scale, causal, kv_lens   as for fa_fwd (kv_lens [B] or NULL)
+ *   workspace     device memory of fa_prenorm_attention_workspace_bytes(B, N, H,
+ *                 H_kv, d) bytes, 256-byte aligned, holding the stages in this
+ *                 order, each starting on a 256-byte boundary: mean [B*N] and
+ *                 rstd [B*N] fp32, qkv [B*N, (H + 2*H_kv)*d] and o [B*N, H*d] in
+ *                 the dtype, lse [B, H, N] fp32 (readable after the call).
+ *
+ * Runs fa_ln_stats, fa_ln_linear (qkv), the attention forward on qkv in place
+ * (fa_fwd_ex strides, o in the dtype), and fa_linear with x as the residual.
+ * d as for fa_fwd_ex; C a multiple of 64; eps, scale, causal as above;
+ * FA_ERR_WORKSPACE for a NULL or short workspace.
+ */
+size_t fa_prenorm_attention_workspace_bytes(int B, int N, int H, int H_kv, int d);
+int fa_prenorm_attention(const void *x, const void *w_qkv_folded, const float *b_qkv_folded,
+                         const float *colsum_qkv, const void *w_o, const float *b_o, void *y, int B,
+                         int N, int H, int H_kv, int d, float eps, float scale, int causal,
+                         const int32_t *kv_lens, int dtype, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /* Workspace bytes fa_decode_paged needs for these sizes (0 for invalid sizes). */
 size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int page_size);

@@ -299,3 +299,155 @@ def call_append(**over):
 ])
 def test_kv_append_argument_checks(lib, over, status):
     assert call_append(**over) == status
+
+
+# ------------------------------------------------------ pre-LN block ---
+# Every case below ends in an error status or an empty call: none launches.
+
+def call_stats(**over):
+    a = dict(x=A, mean=A, rstd=A, T=4, C=64, eps=1e-5, dtype=1, stream=None)
+    a.update(over)
+    return fa.fa_ln_stats(a["x"], a["mean"], a["rstd"], a["T"], a["C"], a["eps"], a["dtype"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), fa.FA_ERR_SHAPE),
+    (dict(C=60), fa.FA_ERR_UNSUPPORTED),
+    (dict(C=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(eps=-1e-5), fa.FA_ERR_ARG),
+    (dict(eps=float("nan")), fa.FA_ERR_ARG),
+    (dict(x=None), fa.FA_ERR_NULL),
+    (dict(rstd=A + 4), fa.FA_ERR_ALIGN),
+    (dict(x=A + 8), fa.FA_ERR_ALIGN),
+    (dict(T=0, x=None, mean=None, rstd=None), fa.FA_OK),
+])
+def test_ln_stats_argument_checks(lib, over, status):
+    assert call_stats(**over) == status
+
+
+def call_fold(**over):
+    a = dict(g=A, b=A, w=A, bias=None, wf=A, bf=A, cs=A, N=24, C=64, dtype=0, stream=None)
+    a.update(over)
+    return fa.fa_ln_fold_weights(a["g"], a["b"], a["w"], a["bias"], a["wf"], a["bf"], a["cs"],
+                                 a["N"], a["C"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(N=-1), fa.FA_ERR_SHAPE),
+    (dict(C=12), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(g=None), fa.FA_ERR_NULL),
+    (dict(cs=None), fa.FA_ERR_NULL),
+    (dict(bias=A + 4), fa.FA_ERR_ALIGN),
+    (dict(wf=A + 2), fa.FA_ERR_ALIGN),
+    (dict(N=0, g=None, b=None, w=None, wf=None, bf=None, cs=None), fa.FA_OK),
+])
+def test_ln_fold_argument_checks(lib, over, status):
+    assert call_fold(**over) == status
+
+
+def call_ln_linear(**over):
+    a = dict(x=A, mean=A, rstd=A, wf=A, bf=A, cs=A, y=A, T=300, C=1024, N=3072, dtype=1,
+             stream=None)
+    a.update(over)
+    return fa.fa_ln_linear(a["x"], a["mean"], a["rstd"], a["wf"], a["bf"], a["cs"], a["y"], a["T"],
+                           a["C"], a["N"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-2), fa.FA_ERR_SHAPE),
+    (dict(C=1000), fa.FA_ERR_UNSUPPORTED),     # k-steps of 64
+    (dict(C=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=3076), fa.FA_ERR_UNSUPPORTED),     # outputs in multiples of 8
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(C=1 << 22), fa.FA_ERR_SHAPE),        # 256 rows x K x 2 bytes past 2^31
+    (dict(T=1 << 30, N=1 << 30), fa.FA_ERR_SHAPE),
+    (dict(mean=None), fa.FA_ERR_NULL),
+    (dict(y=None), fa.FA_ERR_NULL),
+    (dict(cs=A + 4), fa.FA_ERR_ALIGN),
+    (dict(x=A + 8), fa.FA_ERR_ALIGN),
+    (dict(T=0, x=None, y=None), fa.FA_OK),
+    (dict(N=0, wf=None, y=None), fa.FA_OK),
+])
+def test_ln_linear_argument_checks(lib, over, status):
+    assert call_ln_linear(**over) == status
+
+
+def call_linear(**over):
+    a = dict(a=A, w=A, bias=None, res=None, y=A, M=100, K=128, N=64, dtype=0, stream=None)
+    a.update(over)
+    return fa.fa_linear(a["a"], a["w"], a["bias"], a["res"], a["y"], a["M"], a["K"], a["N"],
+                        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(M=-1), fa.FA_ERR_SHAPE),
+    (dict(K=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=12), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(w=None), fa.FA_ERR_NULL),
+    (dict(res=A + 8), fa.FA_ERR_ALIGN),
+    (dict(bias=A + 4), fa.FA_ERR_ALIGN),
+    (dict(y=A + 2), fa.FA_ERR_ALIGN),
+    (dict(M=0, a=None, y=None), fa.FA_OK),
+])
+def test_linear_argument_checks(lib, over, status):
+    assert call_linear(**over) == status
+
+
+def test_prenorm_workspace_size(lib):
+    B, N, H, Hkv, d = 2, 100, 4, 2, 64
+    up = lambda v: (v + 255) // 256 * 256
+    T = B * N
+    want = 2 * up(T * 4) + up(T * (H + 2 * Hkv) * d * 2) + up(T * H * d * 2) + up(B * H * N * 4)
+    assert fa.fa_prenorm_attention_workspace_bytes(B, N, H, Hkv, d) == want
+    assert fa.fa_prenorm_attention_workspace_bytes(-1, N, H, Hkv, d) == 0
+    assert fa.fa_prenorm_attention_workspace_bytes(B, N, H, 3, d) == 0
+
+
+def call_block(**over):
+    a = dict(x=A, wq=A, bq=A, cq=A, wo=A, bo=None, y=A, B=2, N=100, H=4, H_kv=2, d=64, eps=1e-5,
+             scale=0.125, causal=0, kl=None, dtype=1, ws=A, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return fa.fa_prenorm_attention(a["x"], a["wq"], a["bq"], a["cq"], a["wo"], a["bo"], a["y"],
+                                   a["B"], a["N"], a["H"], a["H_kv"], a["d"], a["eps"], a["scale"],
+                                   a["causal"], a["kl"], a["dtype"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+    (dict(H_kv=3), fa.FA_ERR_SHAPE),
+    (dict(H_kv=0), fa.FA_ERR_SHAPE),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=3, H_kv=1, d=48), fa.FA_ERR_UNSUPPORTED),   # C = 144 is not a multiple of 64
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_ARG),
+    (dict(causal=2), fa.FA_ERR_ARG),
+    (dict(N=1 << 20, H=16, H_kv=16), fa.FA_ERR_SHAPE),   # key offsets past 2^31 bytes
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), fa.FA_ERR_WORKSPACE),
+    (dict(x=None), fa.FA_ERR_NULL),
+    (dict(cq=None), fa.FA_ERR_NULL),
+    (dict(ws=A + 16), fa.FA_ERR_ALIGN),
+    (dict(bo=A + 4), fa.FA_ERR_ALIGN),
+    (dict(kl=A + 2), fa.FA_ERR_ALIGN),
+    (dict(y=A + 8), fa.FA_ERR_ALIGN),
+    (dict(B=0, x=None, y=None, ws=None), fa.FA_OK),
+    (dict(N=0, x=None, y=None, ws=None), fa.FA_OK),
+])
+def test_prenorm_attention_argument_checks(lib, over, status):
+    assert call_block(**over) == status
+
+
+def test_block_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.ln_stats(x)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.linear(x, torch.zeros(8, 64, dtype=torch.bfloat16))

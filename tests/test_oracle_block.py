@@ -228,3 +228,58 @@ def test_block_zero_output_weights_is_identity():
     res = ob.prenorm_attention(w.x, "f16", w.gamma, w.beta, w.w_qkv, w.b_qkv, zero,
                                np.zeros(w.C), 1, 7, 2, 2, 16, w.eps, w.scale, False)
     assert np.array_equal(res["y"], gen.bits_to_float(w.x, "f16").astype(np.float64))
+
+
+def test_block_sampled_tokens_match_the_full_block():
+    """The sampled-token form returns the full block's rows for those tokens."""
+    B, N, H, Hkv, d = 2, 9, 4, 2, 16
+    w = gen.block_inputs(B, N, H, d, "bf16", 43, Hkv=Hkv, causal=True, kv_len_range=(3, 9))
+    args = (w.x, "bf16", w.gamma, w.beta, w.w_qkv, w.b_qkv, w.w_o, w.b_o, B, N, H, Hkv, d, w.eps,
+            w.scale, True, w.kv_lens)
+    full = ob.prenorm_attention(*args)
+    tok = np.array([17, 0, 9, 5])
+    part = ob.prenorm_attention(*args, tokens=tok)
+    assert np.array_equal(part["qkv"], full["qkv"])
+    for key in ("o", "o_bits", "y", "oprod"):
+        assert np.array_equal(part[key], full[key][tok]), key
+    lse_full = full["lse"].transpose(0, 2, 1).reshape(B * N, H)
+    assert np.array_equal(part["lse"], lse_full[tok])
+
+
+def test_fold_identity_with_exact_scales():
+    """With gamma a power of two per column, gamma * W is exact in the dtype and
+    the folded layer equals LN(x) W^T + b (the identity the fold rests on)."""
+    w = gen.block_inputs(2, 6, 2, 32, "bf16", 51)
+    rng = np.random.default_rng(3)
+    gamma = (2.0 ** rng.integers(-2, 3, size=w.C)).astype(np.float32)
+    wf, bf = ob.fold_weights(gamma, w.beta, w.w_qkv, w.b_qkv, "bf16")
+    W = gen.bits_to_float(w.w_qkv, "bf16").astype(np.float64)
+    assert np.array_equal(gen.bits_to_float(wf, "bf16").astype(np.float64), W * gamma)
+    y_fold, _ = ob.ln_linear_folded(w.x, "bf16", wf, bf, w.eps)
+    y_def, _, _ = ob.ln_linear(w.x, "bf16", gamma, w.beta, w.w_qkv, w.b_qkv, w.eps)
+    assert np.allclose(y_fold, y_def, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fold_rounds_like_a_float32_product(dtype):
+    """W' is gamma * w formed in float32 and rounded to the dtype: equal to
+    torch's / numpy's rounding of the float32 product."""
+    w = gen.block_inputs(1, 4, 2, 32, dtype, 52)
+    wf, _ = ob.fold_weights(w.gamma, w.beta, w.w_qkv, None, dtype)
+    prod32 = gen.bits_to_float(w.w_qkv, dtype) * w.gamma[None, :]
+    assert prod32.dtype == np.float32
+    assert np.array_equal(wf, gen.round_bits(prod32, dtype))
+
+
+def test_folded_block_close_to_the_definition():
+    """The folded block differs from the definition only by the dtype rounding
+    of gamma W: within u |xhat| . |gamma W| on qkv."""
+    B, N, H, Hkv, d = 2, 8, 2, 1, 32
+    w = gen.block_inputs(B, N, H, d, "f16", 53, Hkv=Hkv)
+    args = (w.x, "f16", w.gamma, w.beta, w.w_qkv, w.b_qkv, w.w_o, w.b_o, B, N, H, Hkv, d, w.eps,
+            w.scale, False)
+    a = ob.prenorm_attention(*args)
+    f = ob.prenorm_attention(*args, folded=True)
+    _, absprod, _ = ob.ln_linear(w.x, "f16", w.gamma, w.beta, w.w_qkv, w.b_qkv, w.eps)
+    assert np.all(np.abs(a["qkv"] - f["qkv"]) <= 2.0 ** -11 * absprod * (1 + 1e-9))
+    assert not np.array_equal(a["qkv"], f["qkv"])
