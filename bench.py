@@ -324,6 +324,71 @@ def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
             "frac": tf / PEAK_BF16_TFLOPS, "flops": flops}
 
 
+BLOCK_WORKLOAD = "prenorm_block_b8_n4096_h16_d64_bf16"
+
+
+def time_block(fa, dev, steps, warmup):
+    """The pre-LayerNorm attention block (fa_prenorm_attention) on its encoder
+    workload, and each of its stages alone (the same kernels through their own
+    entry points): average over `steps` launches with HIP events after
+    `warmup`.  FLOPs: 2 T C (H + 2 H_kv) d for the Q/K/V layer, 2 T C^2 for
+    the output layer, the attention forward's count for the attention."""
+    import torch
+
+    w = gen.block_workload(BLOCK_WORKLOAD)
+    tdt = torch.bfloat16
+    x = gen.to_torch(w.x, w.dtype).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    folded = fa.ln_fold_weights(f32(w.gamma), f32(w.beta), gen.to_torch(w.w_qkv, w.dtype).to(dev),
+                                f32(w.b_qkv))
+    w_o = gen.to_torch(w.w_o, w.dtype).to(dev)
+    b_o = f32(w.b_o)
+    T, C, d, H, Hkv, N, B = w.T, w.C, w.d, w.H, w.Hkv, w.N, w.B
+    R = (H + 2 * Hkv) * d
+    kw = dict(B=B, N=N, H=H, H_kv=Hkv, eps=w.eps, scale=w.scale, causal=w.causal)
+    y, ws = fa.prenorm_attention(x, folded, w_o, b_o, **kw)
+    views = fa.prenorm_workspace_views(ws, B, N, H, Hkv, d, tdt)
+    qkv, o_flat, lse = views["qkv"], views["o"], views["lse"]
+    heads = qkv.view(B, N, H + 2 * Hkv, d)
+    q, k, v = (heads[:, :, :H].transpose(1, 2), heads[:, :, H:H + Hkv].transpose(1, 2),
+               heads[:, :, H + Hkv:].transpose(1, 2))
+    o4 = o_flat.view(B, N, H, d).transpose(1, 2)
+    mean, rstd = views["mean"], views["rstd"]
+    stages = {
+        "ln_stats": lambda: fa.ln_stats(x, w.eps),
+        "qkv_gemm": lambda: fa.ln_linear(x, mean, rstd, folded, out=qkv),
+        "attention": lambda: fa.forward(q, k, v, scale=w.scale, causal=w.causal, out=(o4, lse)),
+        "out_gemm": lambda: fa.linear(o_flat, w_o, b_o, x, out=y),
+        "block": lambda: fa.prenorm_attention(x, folded, w_o, b_o, workspace=ws, out=y, **kw),
+    }
+    res = {}
+    for name, fn in stages.items():
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    fl_qkv = 2.0 * T * C * R
+    fl_out = 2.0 * T * C * C
+    fl_att = attention_flops(B, H, N, N, d, w.causal)
+    tfs = lambda fl, ms: fl / (ms / 1e3) / 1e12
+    out = {"workload": BLOCK_WORKLOAD, "tokens": T, "block_ms": res["block"],
+           "tokens/s": T / (res["block"] / 1e3),
+           "TFLOP/s": tfs(fl_qkv + fl_out + fl_att, res["block"]),
+           "stages_ms": {k: res[k] for k in ("ln_stats", "qkv_gemm", "attention", "out_gemm")},
+           "qkv_gemm_TFLOP/s": tfs(fl_qkv, res["qkv_gemm"]),
+           "out_gemm_TFLOP/s": tfs(fl_out, res["out_gemm"]),
+           "attention_TFLOP/s": tfs(fl_att, res["attention"]),
+           "ln_stats_GB/s": T * C * 2 / (res["ln_stats"] / 1e3) / 1e9}
+    out["qkv_gemm_frac"] = out["qkv_gemm_TFLOP/s"] / PEAK_BF16_TFLOPS
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +404,8 @@ def main():
                     help="skip the backward timed after the steps")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the paged-cache append timed after the steps")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the pre-LayerNorm attention block timed after the steps")
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -512,6 +579,9 @@ def main():
     if not args.no_variants:
         print("[bench] forward variants", file=sys.stderr, flush=True)
         result["variants"] = time_variants(fa, dev, args.steps, args.warmup)
+    if not args.no_block:
+        print("[bench] pre-LayerNorm block", file=sys.stderr, flush=True)
+        result["prenorm_block"] = time_block(fa, dev, args.steps, args.warmup)
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, o.cpu().numpy(), lse.cpu().numpy(),

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(GemmArgs g)
     // [operand: 0 = A, 1 = W][stage]; a tile row is 8 16-byte slots, slot =
     // chunk ^ swz_k(row) so that the MFMA operand reads are conflict-free
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][GM_OPB];
+    __shared__ __attribute__((aligned(16))) float fv[512];   // epilogue: the tile's bias, then colsum
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int tiles_n = (g.N + GM_TILE - 1) / GM_TILE;
@@ -214,6 +215,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(GemmArgs g)
     for (int ks = 0; ks < 4; ++ks)
         rd[ks] = r32 * 128 + (((2 * ks + hh) ^ sw) << 4);
 
+    // the epilogue's per-token statistics, loaded while the k-loop runs
+    int tok[2];
+    float tm[2] = {0.f, 0.f}, tr[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        tok[j] = m0 + wt * 64 + j * 32 + r32;
+        if constexpr (EPI == GEMM_EPI_LN) {
+            if (tok[j] < g.M) {
+                tm[j] = g.mean[tok[j]];
+                tr[j] = g.rstd[tok[j]];
+            }
+        }
+    }
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -221,23 +235,34 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(GemmArgs g)
         for (int j = 0; j < 2; ++j)
             acc[i][j] = f32x16_t{};
 
+    // Operands of k16 step ks + 1 are read while the MFMAs of step ks run
+    // (two register sets); the scheduling barriers keep the compiler from
+    // sinking the reads next to their MFMAs.
     auto compute = [&](int stage) {
         const unsigned char *at = &lds[0][stage][wt * 64 * 128];
         const unsigned char *wtile = &lds[1][stage][wn * 128 * 128];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t wf[4], xf[2];
+        u32x4_t wf[2][4], xf[2][2];
+        auto read = [&](int ks, int buf) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                wf[i] = *reinterpret_cast<const u32x4_t *>(wtile + i * 32 * 128 + rd[ks]);
+                wf[buf][i] = *reinterpret_cast<const u32x4_t *>(wtile + i * 32 * 128 + rd[ks]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                xf[j] = *reinterpret_cast<const u32x4_t *>(at + j * 32 * 128 + rd[ks]);
+                xf[buf][j] = *reinterpret_cast<const u32x4_t *>(at + j * 32 * 128 + rd[ks]);
+        };
+        read(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int buf = ks & 1;
+            if (ks + 1 < 4)
+                read(ks + 1, buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = mma32<BF16>(wf[i], xf[j], acc[i][j]);
+                    acc[i][j] = mma32<BF16>(wf[buf][i], xf[buf][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -260,36 +285,50 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(GemmArgs g)
 
     // epilogue: block (i, j) register r of lane l is feature
     // n0 + 128 wn + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 and token
-    // m0 + 64 wt + 32 j + l % 32; four consecutive features per store
-    int tok[2];
-    float tm[2] = {0.f, 0.f}, tr[2] = {0.f, 0.f};
+    // m0 + 64 wt + 32 j + l % 32.  Every load it needs is issued before its
+    // first store (the output may not alias the inputs): the tile's
+    // per-feature vectors go through LDS, the residual pieces straight into
+    // registers.  The finished 16-bit tile is then staged in LDS (free after
+    // the last k-step) and written out by rows: a store straight from the
+    // accumulator layout would touch 32 output rows per instruction.
+    const float *__restrict__ bias = g.bias;
+    const float *__restrict__ colsum = g.colsum;
+    const uint16_t *__restrict__ res = static_cast<const uint16_t *>(g.res);
+    uint16_t *__restrict__ y = static_cast<uint16_t *>(g.y);
+    {
+        const int t = threadIdx.x;
+        const int n = n0 + (t & 255);
+        const float *src = t < 256 ? bias : colsum;
+        fv[t] = (src && n < g.N) ? src[n] : 0.f;
+    }
+    u32x2_t rv[4][4][2];
+    if constexpr (EPI == GEMM_EPI_BIAS) {
+        if (res) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        tok[j] = m0 + wt * 64 + j * 32 + r32;
-        if constexpr (EPI == GEMM_EPI_LN) {
-            if (tok[j] < g.M) {
-                tm[j] = g.mean[tok[j]];
-                tr[j] = g.rstd[tok[j]];
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + wn * 128 + i * 32 + q * 8 + hh * 4;
+                        rv[i][q][j] = (tok[j] < g.M && n < g.N)
+                                          ? *reinterpret_cast<const u32x2_t *>(res + (size_t)tok[j] * g.N + n)
+                                          : u32x2_t{0u, 0u};
+                    }
         }
     }
-    uint16_t *y = static_cast<uint16_t *>(g.y);
-    const uint16_t *res = static_cast<const uint16_t *>(g.res);
+    __syncthreads();   // every wave is done with the operand tiles; fv is filled
+    // the output tile: 256 rows of 512 bytes, 16-byte slot = chunk ^ (row % 32)
+    unsigned char *ot = &lds[0][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 128 + i * 32 + q * 8 + hh * 4;
-            if (n >= g.N)
-                continue;
-            f32x4_t bv = g.bias ? *reinterpret_cast<const f32x4_t *>(g.bias + n) : f32x4_t{};
-            f32x4_t cv{};
-            if constexpr (EPI == GEMM_EPI_LN)
-                cv = *reinterpret_cast<const f32x4_t *>(g.colsum + n);
+            const int nl = wn * 128 + i * 32 + q * 8 + hh * 4;   // feature within the tile
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t *>(fv + nl);
+            const f32x4_t cv = *reinterpret_cast<const f32x4_t *>(fv + 256 + nl);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                if (tok[j] >= g.M)
-                    continue;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -301,16 +340,30 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(GemmArgs g)
                 }
                 if constexpr (EPI == GEMM_EPI_BIAS) {
                     if (res) {
-                        const u32x2_t rv = *reinterpret_cast<const u32x2_t *>(res + (size_t)tok[j] * g.N + n);
-                        v[0] += lo16<BF16>(rv[0]);
-                        v[1] += hi16<BF16>(rv[0]);
-                        v[2] += lo16<BF16>(rv[1]);
-                        v[3] += hi16<BF16>(rv[1]);
+                        v[0] += lo16<BF16>(rv[i][q][j][0]);
+                        v[1] += hi16<BF16>(rv[i][q][j][0]);
+                        v[2] += lo16<BF16>(rv[i][q][j][1]);
+                        v[3] += hi16<BF16>(rv[i][q][j][1]);
                     }
                 }
-                *reinterpret_cast<u32x2_t *>(y + (size_t)tok[j] * g.N + n) =
+                const int row = wt * 64 + j * 32 + r32;
+                const int slot = (nl >> 3) ^ (row & 31);
+                *reinterpret_cast<u32x2_t *>(ot + row * 512 + slot * 16 + hh * 8) =
                     u32x2_t{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3])};
             }
+        }
+    }
+    __syncthreads();
+    // rows out: wave w writes rows 32 w .. 32 w + 31, two per instruction
+    {
+        const int chunk = lane & 31;
+        const int n = n0 + chunk * 8;
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int row = wave * 32 + it * 2 + hh;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ot + row * 512 + ((chunk ^ (row & 31)) << 4));
+            if (m0 + row < g.M && n < g.N)
+                *reinterpret_cast<u32x4_t *>(y + (size_t)(m0 + row) * g.N + n) = v;
         }
     }
 }
