@@ -406,6 +406,8 @@ def main():
                     help="skip the paged-cache append timed after the steps")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the pre-LayerNorm attention block timed after the steps")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only time the pre-LayerNorm attention block (for its profiles) and exit")
     ap.add_argument("--gqa-only", action="store_true",
                     help="only run the grouped-query decode (for its counter runs) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -438,6 +440,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}), flush=True)
+        return
+    if args.block_only:
+        print(json.dumps({"prenorm_block": time_block(fa, dev, args.steps, args.warmup)}),
+              flush=True)
         return
     if args.gqa_only:
         gq = gen.decode_workload(GQA_WORKLOAD)
