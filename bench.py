@@ -324,6 +324,44 @@ def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
             "frac": tf / PEAK_BF16_TFLOPS, "flops": flops}
 
 
+def time_decode_groups(fa, dev, steps, warmup):
+    """The grouped-query decode batch with wider groups (the S32 H32 d128 batch
+    drawn with 4 K/V heads: 8 query heads each, and with 1: multi-query),
+    which take the matrix-core decode kernel; average over `steps` launches
+    (HIP events), GB/s on the same algorithmic bytes as `decode`."""
+    import torch
+
+    out = {}
+    for hkv in (4, 1):
+        w = gen.decode_workload(GQA_WORKLOAD, Hkv=hkv)
+        kp = gen.build_pool_device(w, "k", dev)
+        vp = gen.build_pool_device(w, "v", dev)
+        q = gen.to_torch(w.q, w.dtype).to(dev)
+        pt = torch.from_numpy(w.page_table).to(dev)
+        kl = torch.from_numpy(w.kv_lens).to(dev)
+        wsb = fa.fa_decode_workspace_bytes(w.S, w.H, w.d, w.page_table.shape[1], 16)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        o = torch.empty((w.S, w.H, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
+        call = lambda: fa.decode_paged(q, kp, vp, pt, kl, scale=w.scale, workspace=ws, out=(o, lse))
+        for _ in range(warmup):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        nb = decode_bytes(w.kv_lens, w.H, w.d, Hkv=hkv)
+        gbs = nb / (ms / 1e3) / 1e9
+        out[f"h32_kv{hkv}"] = {"H": w.H, "H_kv": hkv, "kernel_ms_avg": ms, "bytes": nb, "GB/s": gbs,
+                               "frac": gbs / PEAK_HBM_GBS, "tokens": int(w.kv_lens.sum())}
+        del kp, vp
+    return out
+
+
 BLOCK_WORKLOAD = "prenorm_block_b8_n4096_h16_d64_bf16"
 
 
@@ -579,6 +617,9 @@ def main():
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
         result["backward"] = time_backward(fa, dev, q, k, v, o, lse, w, args.steps, args.warmup)
+    if gq is not None and not args.no_variants:
+        print("[bench] decode with wider query-head groups", file=sys.stderr, flush=True)
+        result["decode_groups"] = time_decode_groups(fa, dev, args.steps, args.warmup)
     if gq is not None and not args.no_append:
         print("[bench] kv append", file=sys.stderr, flush=True)
         result["kv_append"] = time_append(fa, dev, gq, g_kp, g_vp, g_pt, args.steps, args.warmup)

@@ -93,6 +93,8 @@ hipError_t launch_gemm(const GemmArgs &g, int epi, bool bf16, hipStream_t stream
 
 // Decode: cached tokens per split-KV chunk, and the launch.
 constexpr int kDecodeChunkPages = 8;
+// Query heads per K/V head from which decode always uses the matrix-core kernel.
+constexpr int kDecodeMfmaGroup = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

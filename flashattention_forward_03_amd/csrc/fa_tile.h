@@ -236,6 +236,99 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[kBN<D> / 32], int rel)
         }
 }
 
+// ---- online softmax of one 32-key tile (shared by the forward and the
+// grouped-query decode)
+
+// Bound on the probabilities formed against a stale running max, in
+// exponent (log2) units: f16 P must stay below 65504, bf16 has fp32's range.
+template <bool BF16>
+constexpr float kRescaleLog2 = BF16 ? 32.0f : 15.0f;
+// Per-lane online-softmax state.
+struct RowState {
+    float m;    // running max, raw score units (-inf until a key is seen)
+    float l;    // running sum of exp2(s*c - m*c), fp32
+    float mc;   // m*c, or 0 while m is -inf (kept, not recomputed per tile)
+};
+
+// Probabilities of one tile against the row's current (possibly stale) max
+// m: p = exp2(s*c - m*c), packed to 16 bits for the MFMA, summed in fp32
+// (4 independent partial sums).  Returns the row sum of this lane's 32 p.
+template <int NB, bool BF16>
+__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, float c_log2, u32x4_t (&pf)[2 * NB])
+{
+    float ps[4];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * h2 + 2 * q;
+                const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
+                const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
+                pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
+                // the first pair starts each partial sum (no 0 + x: x may be -0)
+                ps[q] = (blk == 0 && h2 == 0) ? p0 + p1 : ps[q] + (p0 + p1);
+            }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// Online softmax step for one tile.  The running max m only has to keep
+// p = exp2(s*c - m*c) below 2^tau (no overflow in the 16-bit P, fp32 sums),
+// and the exact softmax does not depend on which m is used (m cancels in
+// O = sum p v / sum p and LSE = m + ln l).  So the common path does not
+// compute the tile max at all: it forms p against the current m and checks
+// the row sum (sum >= max p); only when some row of the wave exceeds 2^tau,
+// overflowed, or has no finite m yet (its first keys) does the wave take
+// the exact path: tile max, new m = max(m, tile max), rescale of l and O by
+// alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
+// uniform) when O must be multiplied by alpha (done by the caller).
+// (Taking the exact path unconditionally on the first tile instead, so that
+// the check is one compare, measured slower: the extra branch costs spills.)
+template <int D, bool BF16>
+__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
+                                             u32x4_t (&pf)[kBN<D> / 16], float c_log2, float tau_log2,
+                                             float &alpha)
+{
+    const float limit = exp2f(tau_log2);
+    float mc = st.mc;
+    alpha = 1.f;
+    bool rescale = false;
+    // at most two passes: the second one runs against the exact max (p <= 1)
+    for (int pass = 0; pass < 2; ++pass) {
+        const float psum = exp_tile<kBN<D> / 32, BF16>(s, mc, c_log2, pf);
+        const bool bad = pass == 0 && (st.m == -INFINITY || !(psum <= limit));
+        if (__builtin_amdgcn_ballot_w64(bad) == 0) {
+            st.l = fmaf(st.l, alpha, psum);
+            break;
+        }
+        // exact path: tile max (lane-local, then the other half of the wave)
+        float mx = s[0][0];
+#pragma unroll
+        for (int blk = 0; blk < kBN<D> / 32; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[blk][r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float m_new = fmaxf(st.m, mx);
+        // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
+        alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
+        st.m = m_new;
+        mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
+        st.mc = mc;
+        rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+    }
+    return rescale;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alpha)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+        oacc[db] *= alpha;
+}
+
 // s_waitcnt for "at most N vector-memory operations outstanding" (other
 // counters untouched).
 template <int N>

@@ -1,7 +1,10 @@
 """GPU parity of the grouped-query entry points (fa_fwd_gqa, fa_decode_paged_gqa)
 against the fp64 oracle, through the C ABI binding.  Query head h reads K/V
 head h // (H // H_kv): multi-query (H_kv = 1) and grouped-query attention as
-compared in the llm-kernel-lib page's "Ablation Study"."""
+compared in the llm-kernel-lib page's "Ablation Study".  Decode takes the
+matrix-core kernel from 8 query heads per K/V head (and from 4 when there are
+at most 64 (sequence, K/V head) pairs), the dot-product kernel otherwise: the
+cases below cover both."""
 import math
 
 import numpy as np
@@ -85,8 +88,11 @@ def test_gqa_forward_full_size_sampled():
     (3, 16, 2, 64, (1, 1500), "bf16"),    # 8 per K/V head, d = 64
     (3, 6, 2, 128, (20, 530), "bf16"),    # 3 per K/V head (padded slice)
     (2, 12, 2, 64, (200, 300), "f16"),    # 6 per K/V head (padded slice)
-    (3, 16, 1, 128, (1, 900), "bf16"),    # multi-query: two slices of 8 heads
-    (2, 32, 1, 64, (500, 520), "f16"),    # multi-query: four slices of 8 heads
+    (3, 16, 1, 128, (1, 900), "bf16"),    # multi-query, 16 heads
+    (2, 32, 1, 64, (500, 520), "f16"),    # multi-query, 32 heads
+    (2, 64, 1, 128, (100, 700), "bf16"),  # multi-query, 64 heads: two 32-head slices
+    (40, 12, 2, 64, (1, 300), "f16"),     # 6 per K/V head over 80 (seq, K/V head) pairs
+    (40, 8, 2, 128, (1, 300), "bf16"),    # 4 per K/V head over 80 pairs
 ])
 def test_gqa_decode_parity(S, H, Hkv, d, lens, dtype):
     inp = gen.decode_inputs(S, H, d, lens, dtype, seed=8000 + S * 100 + H + Hkv + d,
@@ -151,3 +157,15 @@ def test_gqa_decode_full_batch():
     o, lse = run_decode(inp)
     o_ref, lse_ref = ref_decode(inp)
     print("gqa decode full", compare(o, lse, o_ref, lse_ref, "gqa decode full"), flush=True)
+
+
+@pytest.mark.parametrize("dtype,nan", [("bf16", 0x7FC0), ("f16", 0x7E00)])
+def test_gqa_decode_unused_slots_poisoned_with_nan_do_not_leak(dtype, nan):
+    """Matrix-core decode: the pool slots past each sequence's end (inside its
+    last page) and every unused page hold NaN; rows past the end read as zero."""
+    inp = gen.decode_inputs(5, 16, 128, (1, 700), dtype, seed=8300, page_size=16,
+                            num_pages=512, Hkv=2)
+    o, lse = run_decode(inp, fill_bits=nan)
+    o_ref, lse_ref = ref_decode(inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    compare(o, lse, o_ref, lse_ref, f"gqa poisoned {dtype}")
