@@ -105,20 +105,26 @@ __device__ __forceinline__ void attend_qtile(
         oacc[db] = f32x16_t{};
     RowState st{-INFINITY, 0.f, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
-    const int krow_in_blk = sigma(l32);
+    int ko[G::NBLK][G::KSTEPS];   // K operand read offsets inside a tile
+    qk_offsets<D>(sigma(l32), hh, ko);
     const u32x4s_t krsrc = make_rsrc(Kb, Nk * krs), vrsrc = make_rsrc(Vb, Nk * vrs);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
     unsigned kstep[G::PIECES_PER_WAVE], vstep[G::PIECES_PER_WAVE];
     dma_offsets<D, true>(wave, lane, d, krs, koff, kstep);
     dma_offsets<D, false>(wave, lane, d, vrs, voff, vstep);
 
+    // copies of tile t: buffer resources moved to the tile's first key, so
+    // the lane offsets stay those of tile 0 (keys past Nk are out of range)
+    auto issue = [&](int t, unsigned char *kdst, unsigned char *vdst) {
+        const int kt0 = t * BN;
+        dma_tile_at<D>(rsrc_at(krsrc, (unsigned)kt0 * krs, (Nk - kt0) * (int)krs), koff, kdst, wave);
+        dma_tile_at<D>(rsrc_at(vrsrc, (unsigned)kt0 * vrs, (Nk - kt0) * (int)vrs), voff, vdst, wave);
+    };
     // prologue: the first ST-1 tiles in flight
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
-        if (i < n_tiles) {
-            dma_tile<D>(krsrc, koff, kstep, krs, i * BN, kbuf[i], wave);
-            dma_tile<D>(vrsrc, voff, vstep, vrs, i * BN, vbuf[i], wave);
-        }
+        if (i < n_tiles)
+            issue(i, kbuf[i], vbuf[i]);
 
     // Q after the prologue copies; the empty asm makes the compiler wait for
     // it here, once, instead of at the loop head on every iteration
@@ -143,14 +149,12 @@ __device__ __forceinline__ void attend_qtile(
         else
             wait_vmcnt<0>();
         __syncthreads();
-        if (t + ST - 1 < n_tiles) {
-            dma_tile<D>(krsrc, koff, kstep, krs, (t + ST - 1) * BN, kfill, wave);
-            dma_tile<D>(vrsrc, voff, vstep, vrs, (t + ST - 1) * BN, vfill, wave);
-        }
+        if (t + ST - 1 < n_tiles)
+            issue(t + ST - 1, kfill, vfill);
         if (t < wave_tiles) {
             const int kt0 = t * BN;
             f32x16_t s[G::NBLK];
-            qk_tile<D, BF16>(kc, krow_in_blk, hh, qf, s);
+            qk_tile_at<D, BF16>(kc, ko, qf, s);
             __builtin_amdgcn_sched_barrier(0);
             const bool need_mask = (kt0 + BN > kvlen) || (causal && kt0 + BN - 1 > wave_first_row + dq);
             if (need_mask)

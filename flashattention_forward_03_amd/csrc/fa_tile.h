@@ -144,6 +144,73 @@ __device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *o
     }
 }
 
+// The same copy from a buffer resource that starts at the tile's first row
+// (rsrc_at): the lane offsets off[] are the tile-0 offsets and never change,
+// so a tile costs no vector instruction; rows past the resource's range and
+// the out-of-range padding columns read as zero.
+template <int D>
+__device__ __forceinline__ void dma_tile_at(const u32x4s_t &rsrc, const unsigned *off, unsigned char *dst, int wave)
+{
+    using G = Geometry<D>;
+#pragma unroll
+    for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
+        const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                     :
+                     : "v"(off[u]), "s"(lds_addr), "s"(rsrc)
+                     : "memory", "m0");
+    }
+}
+
+// Buffer resource r moved forward by byte_off with nbytes in range (scalar
+// arithmetic on the 48-bit base).
+__device__ __forceinline__ u32x4s_t rsrc_at(const u32x4s_t &r, unsigned byte_off, int nbytes)
+{
+    const uint64_t base = (((uint64_t)(r[1] & 0xffffu)) << 32 | r[0]) + byte_off;
+    u32x4s_t o;
+    o[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    o[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
+    o[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
+    o[3] = r[3];
+    return o;
+}
+
+// Per-lane byte offsets of the K operand reads of qk_tile inside a tile, one
+// per (32-key block, k-step): loop-invariant, so that each read is one LDS
+// instruction with the tile's base as its immediate offset.
+template <int D>
+__device__ __forceinline__ void qk_offsets(int krow_in_blk, int hh, int (&ko)[kBN<D> / 32][D / 16])
+{
+    using G = Geometry<D>;
+#pragma unroll
+    for (int blk = 0; blk < G::NBLK; ++blk) {
+        const int row = blk * 32 + krow_in_blk;
+        const int sw = swz_k(row);
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            ko[blk][c] = row * G::ROWB + (swz_slot<G::DC>(2 * c + hh, sw) << 4);
+    }
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile_at(const unsigned char *kb, const int (&ko)[kBN<D> / 32][D / 16],
+                                           const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
+{
+    using G = Geometry<D>;
+    u32x4_t ka[G::NBLK][G::KSTEPS];
+#pragma unroll
+    for (int blk = 0; blk < G::NBLK; ++blk)
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            ka[blk][c] = *reinterpret_cast<const u32x4_t *>(kb + ko[blk][c]);
+#pragma unroll
+    for (int c = 0; c < G::KSTEPS; ++c)
+#pragma unroll
+        for (int blk = 0; blk < G::NBLK; ++blk)
+            s[blk] = c == 0 ? mma32<BF16>(ka[blk][c], qf[c], f32x16_t{}) : mma32<BF16>(ka[blk][c], qf[c], s[blk]);
+}
+
 template <int D, bool BF16>
 __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk, int hh,
                                         const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
@@ -297,8 +364,10 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
     // at most two passes: the second one runs against the exact max (p <= 1)
     for (int pass = 0; pass < 2; ++pass) {
         const float psum = exp_tile<kBN<D> / 32, BF16>(s, mc, c_log2, pf);
-        const bool bad = pass == 0 && (st.m == -INFINITY || !(psum <= limit));
-        if (__builtin_amdgcn_ballot_w64(bad) == 0) {
+        // (two ballots of single compares: their masks combine in scalar registers)
+        const bool clean = pass != 0 || (__builtin_amdgcn_ballot_w64(st.m == -INFINITY) == 0 &&
+                                         __builtin_amdgcn_ballot_w64(!(psum <= limit)) == 0);
+        if (clean) {
             st.l = fmaf(st.l, alpha, psum);
             break;
         }
