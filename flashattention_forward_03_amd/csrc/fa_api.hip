@@ -183,7 +183,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const vo
         return FA_ERR_SHAPE;
     if (H > 0 && (H_kv < 1 || H % H_kv != 0))
         return FA_ERR_SHAPE;
-    if (d != 64)
+    if (d != 64 && d != 128)
         return FA_ERR_UNSUPPORTED;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED;
@@ -204,7 +204,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const vo
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4) ||
         !aligned(kv_lens, 4))
         return FA_ERR_ALIGN;
-    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, scale, causal == 1,
+    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, B, H, H_kv, Nq, Nk, d, scale, causal == 1,
                   dtype == FA_DTYPE_BF16, kv_lens};
     const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)

@@ -12,7 +12,7 @@
 // results are bitwise reproducible.  dK and dV of a K/V head sum over the
 // query heads that share it (grouped-query attention).
 //
-// gfx950 mapping (d = 64), both passes on the 32x32x16 MFMA with the same
+// gfx950 mapping (d = 64 or 128), both passes on the 32x32x16 MFMA with the same
 // register chaining as the forward (an accumulator's registers are the next
 // MFMA's B operand once the rows of the first product are permuted by sigma):
 //   * dQ pass: a workgroup = 4 waves x 32 query rows; Q and dO rows are held
@@ -33,7 +33,6 @@
 namespace fa {
 namespace {
 
-constexpr int BWD_D = 64;      // head dim of the backward kernels
 constexpr int BQ = 128;        // query rows per dQ workgroup (32 per wave)
 constexpr int BK = 128;        // keys per dK/dV workgroup (32 per wave)
 constexpr int BT = 32;         // rows per streamed tile
@@ -66,14 +65,13 @@ __global__ __launch_bounds__(NTHREADS) void bwd_delta_kernel(const float *__rest
 
 // ---------------------------------------------------------------- dQ pass ---
 
-template <bool BF16>
-__global__ __launch_bounds__(NTHREADS, 3) void bwd_dq_kernel(
+template <int D, bool BF16>
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
     float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int n_qtiles, float c_log2, float scale,
     int causal_flag, const int32_t *__restrict__ kv_lens)
 {
-    constexpr int D = BWD_D;
     using G = Geometry<D>;
     static_assert(G::BN == BT, "tile rows");
     constexpr int PER = 2 * G::PIECES_PER_WAVE;   // copies per lane per tile (K + V)
@@ -237,14 +235,13 @@ __device__ __forceinline__ void dma_rows32(const u32x4s_t &rsrc, int r0, unsigne
                  : "memory", "m0");
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
+template <int D, bool BF16>
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
     float *__restrict__ dK, float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int n_ktiles, float c_log2,
     float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
-    constexpr int D = BWD_D;
     using G = Geometry<D>;
     static_assert(G::BN == BT, "tile rows");
     constexpr int PER = 2 * G::PIECES_PER_WAVE + 2;   // Q, dO pieces + LSE, D rows
@@ -418,10 +415,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     }
 }
 
-template <bool BF16>
+template <int D, bool BF16>
 hipError_t launch(const BwdArgs &a, hipStream_t stream)
 {
-    constexpr int D = BWD_D;
     const long long rows = (long long)a.B * a.H * a.Nq;
     const int rows_per_wg = NTHREADS / (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
@@ -432,7 +428,7 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
     const float c_log2 = a.scale * kLog2e;
     const int n_ktiles = (a.Nk + BK - 1) / BK;
     if (n_ktiles > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
                            dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
                            (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse, a.delta, a.dk, a.dv, a.H,
                            a.Hkv, a.Nq, a.Nk, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
@@ -441,7 +437,7 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
             return e;
     }
     const int n_qtiles = (a.Nq + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
                        0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        (const uint16_t *)a.dout, a.lse, a.delta, a.dq, a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, c_log2,
                        a.scale, a.causal ? 1 : 0, a.kv_lens);
@@ -460,7 +456,9 @@ long long bwd_grid_size(int B, int H, int Nq, int Nk)
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
 {
-    return a.bf16 ? launch<true>(a, stream) : launch<false>(a, stream);
+    if (a.d == 128)
+        return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+    return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
 }
 
 }  // namespace fa

@@ -165,7 +165,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
  *            share each K/V head); 16-byte aligned
  *   delta    [B, H, Nq] float32, written with D (caller-owned scratch that the
  *            dK/dV and dQ passes read); 4-byte aligned
- *   d        64 (other head dims: FA_ERR_UNSUPPORTED)
+ *   d        64 or 128 (other head dims: FA_ERR_UNSUPPORTED)
  *   scale, causal, kv_lens: as for the forward that produced o and lse.
  *
  * Rows with no valid key get dQ = 0; keys no row sees get dK = dV = 0.  Every

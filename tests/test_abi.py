@@ -253,8 +253,9 @@ def call_bwd(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, do=A + 8), fa.FA_ERR_ALIGN),      # d = 128 passes the head-dim check
     (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
     (dict(H_kv=3), fa.FA_ERR_SHAPE),
     (dict(Nq=-1), fa.FA_ERR_SHAPE),

@@ -1,5 +1,10 @@
 """GPU parity of the attention backward (fa_bwd through the binding) against the
-fp64 oracle's gradients: dQ, dK, dV and the row term D."""
+fp64 oracle's gradients: dQ, dK, dV and the row term D.
+
+The backward's inputs O and LSE come from the oracle's forward (rounded to
+fp32), so each check sees the backward's own arithmetic only; the tests
+marked end-to-end feed it the GPU forward's O and LSE instead, as a training
+step would (their D then also carries the forward's rounding of O)."""
 import math
 
 import numpy as np
@@ -12,14 +17,19 @@ from parity import compare_grad, device_tensors
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, g_bits):
+def _run(w, g_bits, fwd="oracle"):
     import torch
 
     import flashattention_forward_03_amd as fa
 
     q, k, v, kl = device_tensors(w)
     g = gen.to_torch(g_bits, w.dtype).cuda()
-    o, lse = fa.forward(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl)
+    if fwd == "gpu":
+        o, lse = fa.forward(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl)
+    else:
+        o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, w.kv_lens)
+        o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+        lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
     dq, dk, dv, delta = fa.backward(q, k, v, o, lse, g, scale=w.scale, causal=w.causal,
                                     kv_lens=kl)
     torch.cuda.synchronize()
@@ -31,8 +41,8 @@ def _dout(w, seed):
     return gen.round_bits(rng.standard_normal(w.q.shape, dtype=np.float32), w.dtype)
 
 
-def _check(w, g, what, groups=None):
-    got = _run(w, g)
+def _check(w, g, what, groups=None, fwd="oracle"):
+    got = _run(w, g, fwd)
     ref = oracle.attention_bwd(w.q, w.k, w.v, g, w.dtype, w.scale, w.causal, w.kv_lens,
                                groups=groups)
     out = {}
@@ -77,8 +87,37 @@ def test_backward_deterministic():
 
 
 def test_backward_full_size_sampled_heads():
-    """The causal B8 H16 N4096 d64 backward (the launch the bench times); the
-    oracle computes the full gradients of two (batch, head) pairs."""
+    """End-to-end: the causal B8 H16 N4096 d64 backward (the launch the bench
+    times) on the GPU forward's O and LSE; the oracle computes the full
+    gradients of two (batch, head) pairs."""
     w = gen.fwd_workload("fwd_causal_b8h16_n4096_d64_bf16")
     g = _dout(w, 11800)
-    _check(w, g, "bwd full size", groups=[0, 8 * 16 - 1])
+    _check(w, g, "bwd full size", groups=[0, 8 * 16 - 1], fwd="gpu")
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,dtype,causal,lens", [
+    (1, 2, 2, 128, 128, "bf16", True, None),
+    (2, 4, 2, 200, 200, "f16", True, (50, 200)),      # grouped heads, padding
+    (2, 3, 3, 160, 300, "bf16", False, None),          # Nq < Nk, ragged
+    (1, 2, 1, 300, 130, "f16", True, None),            # Nq > Nk: leading rows see nothing
+    (2, 2, 2, 1, 100, "bf16", False, (0, 100)),        # one query row; kv_len 0
+    (1, 1, 1, 64, 5, "bf16", False, None),             # Nk smaller than a tile
+])
+def test_backward_parity_d128(B, H, Hkv, Nq, Nk, dtype, causal, lens):
+    w = gen.fwd_inputs(B, H, Nq, Nk, 128, dtype, seed=12000 + B * 100 + Nq + Nk, causal=causal,
+                       kv_len_range=lens, Hkv=Hkv)
+    _check(w, _dout(w, 12500 + Nq), f"bwd d128 B{B} H{H}/{Hkv} Nq{Nq} Nk{Nk} {dtype} "
+                                    f"causal={causal} lens={lens}")
+
+
+def test_backward_d128_sampled_heads():
+    """A causal B4 H16 N2048 d128 backward; the oracle computes the full
+    gradients of two (batch, head) pairs."""
+    w = gen.fwd_inputs(4, 16, 2048, 2048, 128, "bf16", seed=12900, causal=True)
+    _check(w, _dout(w, 12901), "bwd d128 B4 H16 N2048", groups=[0, 4 * 16 - 1])
+
+
+def test_backward_d128_end_to_end():
+    """End-to-end at d = 128: the GPU forward's O and LSE into the backward."""
+    w = gen.fwd_inputs(2, 4, 250, 250, 128, "bf16", seed=12950, causal=True, Hkv=2)
+    _check(w, _dout(w, 12951), "bwd d128 end-to-end", fwd="gpu")
