@@ -94,6 +94,14 @@ __device__ __forceinline__ void attend_qtile(
     const int n_tiles = (key_end + BN - 1) / BN;
     const int wave_tiles = min(n_tiles, (wave_key_end + BN - 1) / BN);
 
+    // first tile that needs the mask (both conditions only grow with t): the
+    // one that reaches past kvlen, or (causal) whose last key passes the
+    // wave's first row
+    int mask_t = kvlen / BN;
+    if (causal) {
+        const int x1 = wave_first_row + dq + 1;
+        mask_t = min(mask_t, x1 <= 0 ? 0 : x1 / BN);
+    }
     const int qrow = wave_first_row + l32;
     int lim = kvlen;   // keys j < lim are valid for this lane's row
     if (causal)
@@ -113,18 +121,35 @@ __device__ __forceinline__ void attend_qtile(
     dma_offsets<D, true>(wave, lane, d, krs, koff, kstep);
     dma_offsets<D, false>(wave, lane, d, vrs, voff, vstep);
 
-    // copies of tile t: buffer resources moved to the tile's first key, so
-    // the lane offsets stay those of tile 0 (keys past Nk are out of range)
-    auto issue = [&](int t, unsigned char *kdst, unsigned char *vdst) {
-        const int kt0 = t * BN;
-        dma_tile_at<D>(rsrc_at(krsrc, (unsigned)kt0 * krs, (Nk - kt0) * (int)krs), koff, kdst, wave);
-        dma_tile_at<D>(rsrc_at(vrsrc, (unsigned)kt0 * vrs, (Nk - kt0) * (int)vrs), voff, vdst, wave);
+    // Copies of the next tile into ring slot `slot` (tiles are copied in
+    // order): buffer resources at the tile's first key, advanced by one tile
+    // per copy in scalar registers, so the lane offsets stay those of tile 0
+    // (keys past Nk are out of range); ring slots as 32-bit LDS addresses.
+    uint64_t kb_next = ((uint64_t)krsrc[1] << 32) | krsrc[0];
+    uint64_t vb_next = ((uint64_t)vrsrc[1] << 32) | vrsrc[0];
+    uint32_t kr_next = krsrc[2], vr_next = vrsrc[2];
+    const uint32_t kstep_t = (uint32_t)BN * krs, vstep_t = (uint32_t)BN * vrs;
+    uint32_t klds[ST], vlds[ST];
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+        klds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(kbuf[i] + wave * 1024));
+        vlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(vbuf[i] + wave * 1024));
+    }
+    auto issue = [&](int slot) {
+        const u32x4s_t kr = {(uint32_t)kb_next, (uint32_t)(kb_next >> 32), kr_next, krsrc[3]};
+        const u32x4s_t vr = {(uint32_t)vb_next, (uint32_t)(vb_next >> 32), vr_next, vrsrc[3]};
+        dma_tile_lds<D>(kr, koff, klds[slot]);
+        dma_tile_lds<D>(vr, voff, vlds[slot]);
+        kb_next += kstep_t;
+        vb_next += vstep_t;
+        kr_next -= kstep_t;
+        vr_next -= vstep_t;
     };
     // prologue: the first ST-1 tiles in flight
 #pragma unroll
     for (int i = 0; i < ST - 1; ++i)
         if (i < n_tiles)
-            issue(i, kbuf[i], vbuf[i]);
+            issue(i);
 
     // Q after the prologue copies; the empty asm makes the compiler wait for
     // it here, once, instead of at the loop head on every iteration
@@ -139,25 +164,35 @@ __device__ __forceinline__ void attend_qtile(
             asm volatile("" : "+v"(qf[c]));
     }
 
-    // Iteration t: wait for tile t (own loads, then everyone's via the
-    // barrier), refill the ring slot freed by tile t-1 with tile t+ST-1,
-    // then S = K Q^T, masks, online softmax, O += P V on tile t.
-    auto iter = [&](int t, unsigned char *kc, unsigned char *vc, unsigned char *kfill,
-                    unsigned char *vfill) {
+    // Iteration t (tile t in ring slot cur): wait for tile t (own loads,
+    // then everyone's via the barrier), refill slot `fill`, freed by tile
+    // t-1, with tile t+ST-1, then S = K Q^T, masks, online softmax, O += P V
+    // on tile t.  The K operand reads go out before the copy is issued, so
+    // its scalar work overlaps their LDS round trip (d = 128: after it; the
+    // operands held across the copy spill there).
+    auto iter = [&](int t, int cur, int fill) {
+        constexpr bool early = D <= 96;
         if (t + ST - 2 < n_tiles)
             wait_vmcnt<(ST - 2) * PER>();
         else
             wait_vmcnt<0>();
         __syncthreads();
+        const bool comp = t < wave_tiles;
+        u32x4_t ka[G::NBLK][G::KSTEPS];
+        if (early && comp)
+            qk_read<D>(kbuf[cur], ko, ka);
+        __builtin_amdgcn_sched_barrier(0);
         if (t + ST - 1 < n_tiles)
-            issue(t + ST - 1, kfill, vfill);
-        if (t < wave_tiles) {
+            issue(fill);
+        __builtin_amdgcn_sched_barrier(0);
+        if (comp) {
             const int kt0 = t * BN;
             f32x16_t s[G::NBLK];
-            qk_tile_at<D, BF16>(kc, ko, qf, s);
+            if (!early)
+                qk_read<D>(kbuf[cur], ko, ka);
+            qk_mma<D, BF16>(ka, qf, s);
             __builtin_amdgcn_sched_barrier(0);
-            const bool need_mask = (kt0 + BN > kvlen) || (causal && kt0 + BN - 1 > wave_first_row + dq);
-            if (need_mask)
+            if (t >= mask_t)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
             float alpha;
@@ -165,28 +200,28 @@ __device__ __forceinline__ void attend_qtile(
                 rescale_acc<D>(oacc, alpha);
             // keep the V operand reads after the softmax (register pressure)
             __builtin_amdgcn_sched_barrier(0);
-            pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
+            pv_tile<D, BF16>(vbuf[cur], lane, hh, pf, oacc);
         }
     };
 
     int t = 0;
     if constexpr (ST == 3) {
         for (; t + 2 < n_tiles; t += 3) {
-            iter(t, kbuf[0], vbuf[0], kbuf[2], vbuf[2]);
-            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
-            iter(t + 2, kbuf[2], vbuf[2], kbuf[1], vbuf[1]);
+            iter(t, 0, 2);
+            iter(t + 1, 1, 0);
+            iter(t + 2, 2, 1);
         }
         if (t < n_tiles)
-            iter(t, kbuf[0], vbuf[0], kbuf[2], vbuf[2]);
+            iter(t, 0, 2);
         if (t + 1 < n_tiles)
-            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+            iter(t + 1, 1, 0);
     } else {
         for (; t + 1 < n_tiles; t += 2) {
-            iter(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
-            iter(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+            iter(t, 0, 1);
+            iter(t + 1, 1, 0);
         }
         if (t < n_tiles)
-            iter(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
+            iter(t, 0, 1);
     }
     __syncthreads();   // the ring is reused by the next query tile of this workgroup
 

@@ -144,36 +144,25 @@ __device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *o
     }
 }
 
-// The same copy from a buffer resource that starts at the tile's first row
-// (rsrc_at): the lane offsets off[] are the tile-0 offsets and never change,
-// so a tile costs no vector instruction; rows past the resource's range and
-// the out-of-range padding columns read as zero.
+// The same copy from a buffer resource that starts at the tile's first row:
+// the lane offsets off[] are the tile-0 offsets and never change, so a tile
+// costs no vector instruction; rows past the resource's range and the
+// out-of-range padding columns read as zero.  lds is the 32-bit LDS address
+// of this wave's piece 0 in the ring slot (piece u is 4 KB further), so no
+// generic-pointer conversion runs per copy.  The caller moves the resource
+// from tile to tile in scalar registers (base + tile bytes, range - tile
+// bytes); device addresses stay below 2^48, so the high base word never
+// carries into the stride field.
 template <int D>
-__device__ __forceinline__ void dma_tile_at(const u32x4s_t &rsrc, const unsigned *off, unsigned char *dst, int wave)
+__device__ __forceinline__ void dma_tile_lds(const u32x4s_t &r, const unsigned *off, uint32_t lds)
 {
     using G = Geometry<D>;
 #pragma unroll
-    for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
-        const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
+    for (int u = 0; u < G::PIECES_PER_WAVE; ++u)
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                      :
-                     : "v"(off[u]), "s"(lds_addr), "s"(rsrc)
+                     : "v"(off[u]), "s"(lds + (uint32_t)(u * 4 * 1024)), "s"(r)
                      : "memory", "m0");
-    }
-}
-
-// Buffer resource r moved forward by byte_off with nbytes in range (scalar
-// arithmetic on the 48-bit base).
-__device__ __forceinline__ u32x4s_t rsrc_at(const u32x4s_t &r, unsigned byte_off, int nbytes)
-{
-    const uint64_t base = (((uint64_t)(r[1] & 0xffffu)) << 32 | r[0]) + byte_off;
-    u32x4s_t o;
-    o[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    o[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
-    o[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
-    o[3] = r[3];
-    return o;
 }
 
 // Per-lane byte offsets of the K operand reads of qk_tile inside a tile, one
@@ -193,17 +182,26 @@ __device__ __forceinline__ void qk_offsets(int krow_in_blk, int hh, int (&ko)[kB
     }
 }
 
-template <int D, bool BF16>
-__device__ __forceinline__ void qk_tile_at(const unsigned char *kb, const int (&ko)[kBN<D> / 32][D / 16],
-                                           const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
+// S = K Q^T of one tile with the offsets of qk_offsets, in two halves (the
+// K operand reads, then the MFMAs) so that other work can sit between the
+// reads and their first use.
+template <int D>
+__device__ __forceinline__ void qk_read(const unsigned char *kb, const int (&ko)[kBN<D> / 32][D / 16],
+                                        u32x4_t (&ka)[kBN<D> / 32][D / 16])
 {
     using G = Geometry<D>;
-    u32x4_t ka[G::NBLK][G::KSTEPS];
 #pragma unroll
     for (int blk = 0; blk < G::NBLK; ++blk)
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c)
             ka[blk][c] = *reinterpret_cast<const u32x4_t *>(kb + ko[blk][c]);
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_mma(const u32x4_t (&ka)[kBN<D> / 32][D / 16], const u32x4_t (&qf)[D / 16],
+                                       f32x16_t (&s)[kBN<D> / 32])
+{
+    using G = Geometry<D>;
 #pragma unroll
     for (int c = 0; c < G::KSTEPS; ++c)
 #pragma unroll
@@ -358,20 +356,16 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
                                              float &alpha)
 {
     const float limit = exp2f(tau_log2);
-    float mc = st.mc;
     alpha = 1.f;
     bool rescale = false;
-    // at most two passes: the second one runs against the exact max (p <= 1)
-    for (int pass = 0; pass < 2; ++pass) {
-        const float psum = exp_tile<kBN<D> / 32, BF16>(s, mc, c_log2, pf);
-        // (two ballots of single compares: their masks combine in scalar registers)
-        const bool clean = pass != 0 || (__builtin_amdgcn_ballot_w64(st.m == -INFINITY) == 0 &&
-                                         __builtin_amdgcn_ballot_w64(!(psum <= limit)) == 0);
-        if (clean) {
-            st.l = fmaf(st.l, alpha, psum);
-            break;
-        }
-        // exact path: tile max (lane-local, then the other half of the wave)
+    float psum = exp_tile<kBN<D> / 32, BF16>(s, st.mc, c_log2, pf);
+    // (two ballots of single compares: their masks combine in scalar
+    // registers; the exact path is marked unlikely for the code layout)
+    const bool clean = __builtin_amdgcn_ballot_w64(st.m == -INFINITY) == 0 &&
+                       __builtin_amdgcn_ballot_w64(!(psum <= limit)) == 0;
+    if (__builtin_expect(!clean, 0)) {
+        // exact path: tile max (lane-local, then the other half of the wave),
+        // then p again against the new max (p <= 1)
         float mx = s[0][0];
 #pragma unroll
         for (int blk = 0; blk < kBN<D> / 32; ++blk)
@@ -383,10 +377,11 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
         // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
         alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
         st.m = m_new;
-        mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
-        st.mc = mc;
+        st.mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
         rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+        psum = exp_tile<kBN<D> / 32, BF16>(s, st.mc, c_log2, pf);
     }
+    st.l = fmaf(st.l, alpha, psum);
     return rescale;
 }
 
