@@ -111,7 +111,7 @@ __device__ __forceinline__ void attend_qtile(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    RowState st{-INFINITY, 0.f, 0.f};
+    RowState st{-INFINITY, 0.f, -INFINITY};
     const float tau_log2 = kRescaleLog2<BF16>;
     int ko[G::NBLK][G::KSTEPS];   // K operand read offsets inside a tile
     qk_offsets<D>(sigma(l32), hh, ko);

@@ -312,7 +312,7 @@ constexpr float kRescaleLog2 = BF16 ? 32.0f : 15.0f;
 struct RowState {
     float m;    // running max, raw score units (-inf until a key is seen)
     float l;    // running sum of exp2(s*c - m*c), fp32
-    float mc;   // m*c, or 0 while m is -inf (kept, not recomputed per tile)
+    float mc;   // m*c, or -inf while m is -inf (kept, not recomputed per tile)
 };
 
 // Probabilities of one tile against the row's current (possibly stale) max
@@ -347,9 +347,9 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
 // overflowed, or has no finite m yet (its first keys) does the wave take
 // the exact path: tile max, new m = max(m, tile max), rescale of l and O by
 // alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
-// uniform) when O must be multiplied by alpha (done by the caller).
-// (Taking the exact path unconditionally on the first tile instead, so that
-// the check is one compare, measured slower: the extra branch costs spills.)
+// uniform) when O must be multiplied by alpha (done by the caller).  The
+// no-finite-m case needs no compare of its own: mc is -inf then, which makes
+// the row sum +inf or NaN.
 template <int D, bool BF16>
 __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
                                              u32x4_t (&pf)[kBN<D> / 16], float c_log2, float tau_log2,
@@ -358,12 +358,11 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
     const float limit = exp2f(tau_log2);
     alpha = 1.f;
     bool rescale = false;
+    // While m is -inf, mc is -inf too, so p = exp2(s*c + inf) is +inf (or
+    // NaN for a masked score) and the one compare below sends the row to the
+    // exact path; the exact path is marked unlikely for the code layout.
     float psum = exp_tile<kBN<D> / 32, BF16>(s, st.mc, c_log2, pf);
-    // (two ballots of single compares: their masks combine in scalar
-    // registers; the exact path is marked unlikely for the code layout)
-    const bool clean = __builtin_amdgcn_ballot_w64(st.m == -INFINITY) == 0 &&
-                       __builtin_amdgcn_ballot_w64(!(psum <= limit)) == 0;
-    if (__builtin_expect(!clean, 0)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(psum <= limit)) != 0, 0)) {
         // exact path: tile max (lane-local, then the other half of the wave),
         // then p again against the new max (p <= 1)
         float mx = s[0][0];
@@ -377,9 +376,10 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
         // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
         alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
         st.m = m_new;
-        st.mc = m_new == -INFINITY ? 0.f : m_new * c_log2;
+        st.mc = m_new * c_log2;
         rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
-        psum = exp_tile<kBN<D> / 32, BF16>(s, st.mc, c_log2, pf);
+        // (a row with no key yet: p = exp2(-inf - 0) = 0)
+        psum = exp_tile<kBN<D> / 32, BF16>(s, m_new == -INFINITY ? 0.f : st.mc, c_log2, pf);
     }
     st.l = fmaf(st.l, alpha, psum);
     return rescale;
