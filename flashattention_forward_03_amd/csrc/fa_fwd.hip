@@ -64,6 +64,11 @@ __device__ __forceinline__ void store_o4(void *row, int dim0, int o_kind, float 
     }
 }
 
+template <bool B>
+struct LoopTag {
+    static constexpr bool value = B;
+};
+
 // One query tile (BM rows of one (b, h)) against its key tiles.  Qb, Kb, Vb,
 // Ob, LSEb point at row 0 of this (b, h); qsn / osn are row strides in
 // elements, krs / vrs in bytes.
@@ -170,19 +175,23 @@ __device__ __forceinline__ void attend_qtile(
     // on tile t.  The K operand reads go out before the copy is issued, so
     // its scalar work overlaps their LDS round trip (d = 128: after it; the
     // operands held across the copy spill there).
-    auto iter = [&](int t, int cur, int fill) {
+    // With the fast tag the caller guarantees that this wave computes tile
+    // t, that the tile needs no mask and that tile t+ST-1 exists, so the
+    // iteration takes none of those checks.
+    auto iter = [&](int t, int cur, int fill, auto fast_tag) {
+        constexpr bool fast = decltype(fast_tag)::value;
         constexpr bool early = D <= 96;
-        if (t + ST - 2 < n_tiles)
+        if (fast || t + ST - 2 < n_tiles)
             wait_vmcnt<(ST - 2) * PER>();
         else
             wait_vmcnt<0>();
         __syncthreads();
-        const bool comp = t < wave_tiles;
+        const bool comp = fast || t < wave_tiles;
         u32x4_t ka[G::NBLK][G::KSTEPS];
         if (early && comp)
             qk_read<D>(kbuf[cur], ko, ka);
         __builtin_amdgcn_sched_barrier(0);
-        if (t + ST - 1 < n_tiles)
+        if (fast || t + ST - 1 < n_tiles)
             issue(fill);
         __builtin_amdgcn_sched_barrier(0);
         if (comp) {
@@ -192,7 +201,7 @@ __device__ __forceinline__ void attend_qtile(
                 qk_read<D>(kbuf[cur], ko, ka);
             qk_mma<D, BF16>(ka, qf, s);
             __builtin_amdgcn_sched_barrier(0);
-            if (t >= mask_t)
+            if (!fast && t >= mask_t)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
             float alpha;
@@ -204,24 +213,38 @@ __device__ __forceinline__ void attend_qtile(
         }
     };
 
+    // Tiles below fast_end run the check-free iteration; every wave still
+    // passes one barrier per tile, whichever loop it is in.
+    const LoopTag<true> F;
+    const LoopTag<false> C;
+    const int fast_end = min(min(n_tiles - (ST - 1), wave_tiles), mask_t);
     int t = 0;
     if constexpr (ST == 3) {
+        for (; t + 2 < fast_end; t += 3) {
+            iter(t, 0, 2, F);
+            iter(t + 1, 1, 0, F);
+            iter(t + 2, 2, 1, F);
+        }
         for (; t + 2 < n_tiles; t += 3) {
-            iter(t, 0, 2);
-            iter(t + 1, 1, 0);
-            iter(t + 2, 2, 1);
+            iter(t, 0, 2, C);
+            iter(t + 1, 1, 0, C);
+            iter(t + 2, 2, 1, C);
         }
         if (t < n_tiles)
-            iter(t, 0, 2);
+            iter(t, 0, 2, C);
         if (t + 1 < n_tiles)
-            iter(t + 1, 1, 0);
+            iter(t + 1, 1, 0, C);
     } else {
+        for (; t + 1 < fast_end; t += 2) {
+            iter(t, 0, 1, F);
+            iter(t + 1, 1, 0, F);
+        }
         for (; t + 1 < n_tiles; t += 2) {
-            iter(t, 0, 1);
-            iter(t + 1, 1, 0);
+            iter(t, 0, 1, C);
+            iter(t + 1, 1, 0, C);
         }
         if (t < n_tiles)
-            iter(t, 0, 1);
+            iter(t, 0, 1, C);
     }
     __syncthreads();   // the ring is reused by the next query tile of this workgroup
 
