@@ -26,6 +26,8 @@
 //     through the ring.  Per tile: S = Q K^T and dP = dO V^T with a lane
 //     owning a key column, P and dS with the rows' LSE / D read from LDS,
 //     then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+#include <climits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 #include "fa_tile.h"
@@ -121,12 +123,31 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         vstep[G::PIECES_PER_WAVE];
     dma_offsets<D, true>(wave, lane, D, G::ROWB, koff, kstep);   // both tiles are read by rows
     dma_offsets<D, true>(wave, lane, D, G::ROWB, voff, vstep);
+    // copies of the next tile (in order) into ring slot st: resources at the
+    // tile's first key, advanced by one tile per copy in scalar registers
+    uint64_t kb_next = ((uint64_t)krs[1] << 32) | krs[0];
+    uint64_t vb_next = ((uint64_t)vrs[1] << 32) | vrs[0];
+    uint32_t range_next = krs[2];
+    constexpr uint32_t kTileBytes = (uint32_t)BT * G::ROWB;
+    uint32_t klds[STAGES], vlds[STAGES];
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i) {
+        klds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(kring[i] + wave * 1024));
+        vlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(vring[i] + wave * 1024));
+    }
+    auto issue = [&](int st) {
+        const u32x4s_t kr = {(uint32_t)kb_next, (uint32_t)(kb_next >> 32), range_next, krs[3]};
+        const u32x4s_t vr = {(uint32_t)vb_next, (uint32_t)(vb_next >> 32), range_next, vrs[3]};
+        dma_tile_lds<D>(kr, koff, klds[st]);
+        dma_tile_lds<D>(vr, voff, vlds[st]);
+        kb_next += kTileBytes;
+        vb_next += kTileBytes;
+        range_next -= kTileBytes;
+    };
 #pragma unroll
     for (int i = 0; i < STAGES - 1; ++i)
-        if (i < n_tiles) {
-            dma_tile<D>(krs, koff, kstep, G::ROWB, i * BT, kring[i], wave);
-            dma_tile<D>(vrs, voff, vstep, G::ROWB, i * BT, vring[i], wave);
-        }
+        if (i < n_tiles)
+            issue(i);
 
     // Q and dO rows of this lane's query (B operands), its LSE and D
     u32x4_t qf[G::KSTEPS], gf[G::KSTEPS];
@@ -159,25 +180,42 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         acc[db] = f32x16_t{};
-    const int krow = sigma(l32);
+    int ko[G::NBLK][G::KSTEPS];   // K (and V) operand read offsets inside a tile
+    qk_offsets<D>(sigma(l32), hh, ko);
+    // first tile that needs the mask (both conditions only grow with t)
+    int mask_t = kvlen / BT;
+    if (causal) {
+        const int x1 = wave_first_row + dq + 1;
+        mask_t = min(mask_t, x1 <= 0 ? 0 : x1 / BT);
+    }
 
-    auto iter = [&](int t, int cur, int fill) {
-        if (t + STAGES - 2 < n_tiles)
+    // As the forward: the K and V operand reads go out before the next copy
+    // is issued; with the fast tag the caller guarantees the wave computes
+    // tile t unmasked and tile t+STAGES-1 exists, so no per-tile test runs.
+    auto iter = [&](int t, int cur, int fill, auto fast_tag) {
+        constexpr bool fast = decltype(fast_tag)::value;
+        if (fast || t + STAGES - 2 < n_tiles)
             wait_vmcnt<(STAGES - 2) * PER>();
         else
             wait_vmcnt<0>();
         __syncthreads();
-        if (t + STAGES - 1 < n_tiles) {
-            dma_tile<D>(krs, koff, kstep, G::ROWB, (t + STAGES - 1) * BT, kring[fill], wave);
-            dma_tile<D>(vrs, voff, vstep, G::ROWB, (t + STAGES - 1) * BT, vring[fill], wave);
+        const bool comp = fast || t < wave_tiles;
+        u32x4_t ka0[G::NBLK][G::KSTEPS], va0[G::NBLK][G::KSTEPS];
+        if (comp) {
+            qk_read<D>(kring[cur], ko, ka0);
+            qk_read<D>(vring[cur], ko, va0);
         }
-        if (t < wave_tiles) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (fast || t + STAGES - 1 < n_tiles)
+            issue(fill);
+        __builtin_amdgcn_sched_barrier(0);
+        if (comp) {
             const int kt0 = t * BT;
             f32x16_t s[1], dp[1];
-            qk_tile<D, BF16>(kring[cur], krow, hh, qf, s);    // S^T = K Q^T
-            qk_tile<D, BF16>(vring[cur], krow, hh, gf, dp);   // dP^T = V dO^T
+            qk_mma<D, BF16>(ka0, qf, s);    // S^T = K Q^T
+            qk_mma<D, BF16>(va0, gf, dp);   // dP^T = V dO^T
             __builtin_amdgcn_sched_barrier(0);
-            if ((kt0 + BT > kvlen) || (causal && kt0 + BT - 1 > wave_first_row + dq))
+            if (!fast && t >= mask_t)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             // P^T and dS^T, packed to 16 bits as the B operand of dQ^T += K^T dS^T
             u32x4_t dsf[2];
@@ -196,16 +234,24 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
             pv_mfma<D, BF16>(ka, dsf, acc);
         }
     };
+    const LoopTag<true> F;
+    const LoopTag<false> C;
+    const int fast_end = min(min(n_tiles - (STAGES - 1), wave_tiles), mask_t);
     int t = 0;
+    for (; t + 2 < fast_end; t += 3) {
+        iter(t, 0, 2, F);
+        iter(t + 1, 1, 0, F);
+        iter(t + 2, 2, 1, F);
+    }
     for (; t + 2 < n_tiles; t += 3) {
-        iter(t, 0, 2);
-        iter(t + 1, 1, 0);
-        iter(t + 2, 2, 1);
+        iter(t, 0, 2, C);
+        iter(t + 1, 1, 0, C);
+        iter(t + 2, 2, 1, C);
     }
     if (t < n_tiles)
-        iter(t, 0, 2);
+        iter(t, 0, 2, C);
     if (t + 1 < n_tiles)
-        iter(t + 1, 1, 0);
+        iter(t + 1, 1, 0, C);
     __syncthreads();
 
     if (qrow < Nq) {
@@ -222,16 +268,15 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
 
 // ------------------------------------------------------------- dK/dV pass ---
 
-// Copy 32 consecutive fp32 values (a tile's LSE or D) into this wave's LDS
-// slot: lanes 0..31 load one dword each, lanes 32..63 read out of range
-// (zero) into the slot's unused half.
-__device__ __forceinline__ void dma_rows32(const u32x4s_t &rsrc, int r0, unsigned char *dst, int lane)
+// Copy 32 consecutive fp32 values (a tile's LSE or D rows, from the
+// resource's first row) into this wave's LDS slot at 32-bit address lds:
+// lanes 0..31 load one dword each (voff = 4 * lane), lanes 32..63 read out
+// of range (zero) into the slot's unused half.
+__device__ __forceinline__ void dma_dword_lds(const u32x4s_t &rsrc, unsigned voff, uint32_t lds)
 {
-    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)dst);
-    const uint32_t voff = lane < 32 ? (unsigned)(r0 + lane) * 4u : kOutOfRange;
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
                  :
-                 : "v"(voff), "s"(lds_addr), "s"(rsrc)
+                 : "v"(voff), "s"(lds), "s"(rsrc)
                  : "memory", "m0");
 }
 
@@ -294,27 +339,60 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         }
     }
 
-    unsigned qoff[G::PIECES_PER_WAVE], goff[G::PIECES_PER_WAVE], qstep[G::PIECES_PER_WAVE],
-        gstep[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff, qstep);
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, goff, gstep);
-    auto issue = [&](int i, int st) {   // copy (query head, tile) pair i into ring slot st
-        const int hq = kvh * grp + i / n_qt;
-        const int r0 = (qt_begin + i % n_qt) * BT;
-        const size_t rowbase = ((size_t)b * H + hq) * Nq;
-        const u32x4s_t qrs = make_rsrc(Q + rowbase * D, Nq * G::ROWB);
-        const u32x4s_t grs = make_rsrc(dO + rowbase * D, Nq * G::ROWB);
-        const u32x4s_t lrs = make_rsrc(LSE + rowbase, Nq * 4);
-        const u32x4s_t drs = make_rsrc(delta + rowbase, Nq * 4);
-        dma_tile<D>(qrs, qoff, qstep, G::ROWB, r0, qring[st], wave);
-        dma_tile<D>(grs, goff, gstep, G::ROWB, r0, gring[st], wave);
-        dma_rows32(lrs, r0, sring[st][wave][0], lane);
-        dma_rows32(drs, r0, sring[st][wave][1], lane);
+    // Copies stream the (query head, query tile) pairs in order: pair i is
+    // head j = i / n_qt of the group and tile qi = i % n_qt.  The buffer
+    // resources sit at the next pair's first row and advance by one tile per
+    // copy in scalar registers (re-based when the head changes), so the lane
+    // offsets are the tile-0 ones and no division runs per tile.
+    unsigned qoff[G::PIECES_PER_WAVE], qstep[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff, qstep);   // Q and dO tiles: same row layout
+    const unsigned roff = lane < 32 ? (unsigned)lane * 4u : kOutOfRange;
+    uint32_t qlds[STAGES], glds[STAGES], llds[STAGES], dlds[STAGES];
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i) {
+        qlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(qring[i] + wave * 1024));
+        glds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(gring[i] + wave * 1024));
+        llds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)sring[i][wave][0]);
+        dlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)sring[i][wave][1]);
+    }
+    u32x4s_t qr, gr, lr, dr;
+    int nx_qi = 0, nx_j = 0;   // the next pair to copy
+    auto set_head = [&](int j) {
+        const size_t row0 = ((size_t)b * H + kvh * grp + j) * Nq + (size_t)qt_begin * BT;
+        const int rows = Nq - qt_begin * BT;
+        qr = make_rsrc(Q + row0 * D, rows * G::ROWB);
+        gr = make_rsrc(dO + row0 * D, rows * G::ROWB);
+        lr = make_rsrc(LSE + row0, rows * 4);
+        dr = make_rsrc(delta + row0, rows * 4);
+    };
+    auto advance = [](u32x4s_t &r, uint32_t bytes) {
+        const uint64_t base = (((uint64_t)r[1]) << 32 | r[0]) + bytes;
+        r[0] = (uint32_t)base;
+        r[1] = (uint32_t)(base >> 32);
+        r[2] -= bytes;
+    };
+    if (n_tiles > 0)
+        set_head(0);
+    auto issue = [&](int st) {   // copy the next pair into ring slot st
+        dma_tile_lds<D>(qr, qoff, qlds[st]);
+        dma_tile_lds<D>(gr, qoff, glds[st]);
+        dma_dword_lds(lr, roff, llds[st]);
+        dma_dword_lds(dr, roff, dlds[st]);
+        if (++nx_qi == n_qt) {
+            nx_qi = 0;
+            if (++nx_j < grp)
+                set_head(nx_j);
+        } else {
+            advance(qr, BT * G::ROWB);
+            advance(gr, BT * G::ROWB);
+            advance(lr, BT * 4);
+            advance(dr, BT * 4);
+        }
     };
 #pragma unroll
     for (int i = 0; i < STAGES - 1; ++i)
         if (i < n_tiles)
-            issue(i, i);
+            issue(i);
 #pragma unroll
     for (int c = 0; c < G::KSTEPS; ++c) {
         asm volatile("" : "+v"(kf[c]));
@@ -329,7 +407,10 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     const int qrow_perm = sigma(l32);
     const int lim_key = min(kvlen, Nk);
+    // rows this lane's key is visible to: [row_lo, Nq), none past the key range
+    const int row_lo = key >= lim_key ? INT_MAX : (causal ? key - dq : INT_MIN);
 
+    int cur_qi = 0;   // tile index of the pair being computed
     auto iter = [&](int t, int cur, int fill) {
         if (t + STAGES - 2 < n_tiles)
             wait_vmcnt<(STAGES - 2) * PER>();
@@ -337,8 +418,10 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             wait_vmcnt<0>();
         __syncthreads();
         if (t + STAGES - 1 < n_tiles)
-            issue(t + STAGES - 1, fill);
-        const int q0 = (qt_begin + t % n_qt) * BT;
+            issue(fill);
+        const int q0 = (qt_begin + cur_qi) * BT;
+        if (++cur_qi == n_qt)
+            cur_qi = 0;
         // wave-uniform: does any query of this tile see any key of this wave?
         const bool live = kw0 < lim_key && (!causal || kw0 <= q0 + BT - 1 + dq);
         if (live) {
@@ -349,36 +432,42 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             // this lane's rows: register r is query q0 + 16*(r/8) + 8*hh + r%8
             const float *ls = reinterpret_cast<const float *>(sring[cur][wave][0]);
             const float *ds = reinterpret_cast<const float *>(sring[cur][wave][1]);
-            // wave-uniform: may any element of this block be masked?
-            const bool edge = kw0 + 32 > lim_key || q0 + BT > Nq || (causal && kw0 + 31 > q0 + dq);
-            u32x4_t pf[2], dsf[2];
+            float p[16], dsv[16];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const f32x4_t la = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh);
                 const f32x4_t lb = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh + 4);
                 const f32x4_t da = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh);
                 const f32x4_t dbv = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh + 4);
-                float p[8], dsv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int r = 8 * h2 + e;
                     const float lse = e < 4 ? la[e] : lb[e - 4];
                     const float dd = e < 4 ? da[e] : dbv[e - 4];
-                    float pe = fast_exp2(fmaf(s[0][r], c_log2, -lse * kLog2e));
-                    if (edge) {
-                        const int qi = q0 + 16 * h2 + 8 * hh + e;
-                        const bool vis = key < lim_key && qi < Nq && (!causal || key <= qi + dq);
-                        pe = vis ? pe : 0.f;
-                    }
-                    p[e] = pe;
-                    dsv[e] = pe * (dp[0][r] - dd);
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    pf[h2][q] = pack2<BF16>(p[2 * q], p[2 * q + 1]);
-                    dsf[h2][q] = pack2<BF16>(dsv[2 * q], dsv[2 * q + 1]);
+                    p[r] = fast_exp2(fmaf(s[0][r], c_log2, -lse * kLog2e));
+                    dsv[r] = p[r] * (dp[0][r] - dd);
                 }
             }
+            // wave-uniform: may any element of this block be masked?  (p and
+            // dS both zeroed: a row with no visible key has LSE = -inf)
+            const bool edge = kw0 + 32 > lim_key || q0 + BT > Nq || (causal && kw0 + 31 > q0 + dq);
+            if (edge) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = q0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+                    const bool vis = qi >= row_lo && qi < Nq;
+                    p[r] = vis ? p[r] : 0.f;
+                    dsv[r] = vis ? dsv[r] : 0.f;
+                }
+            }
+            u32x4_t pf[2], dsf[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pf[h2][q] = pack2<BF16>(p[8 * h2 + 2 * q], p[8 * h2 + 2 * q + 1]);
+                    dsf[h2][q] = pack2<BF16>(dsv[8 * h2 + 2 * q], dsv[8 * h2 + 2 * q + 1]);
+                }
             __builtin_amdgcn_sched_barrier(0);
             u32x4_t ta[G::DB][G::PCH];
             pv_operands<D, true>(gring[cur], lane, hh, ta);   // dO^T

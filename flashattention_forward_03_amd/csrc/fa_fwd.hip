@@ -64,11 +64,6 @@ __device__ __forceinline__ void store_o4(void *row, int dim0, int o_kind, float 
     }
 }
 
-template <bool B>
-struct LoopTag {
-    static constexpr bool value = B;
-};
-
 // One query tile (BM rows of one (b, h)) against its key tiles.  Qb, Kb, Vb,
 // Ob, LSEb point at row 0 of this (b, h); qsn / osn are row strides in
 // elements, krs / vrs in bytes.

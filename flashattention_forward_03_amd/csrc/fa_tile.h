@@ -393,6 +393,13 @@ __device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alph
         oacc[db] *= alpha;
 }
 
+// Compile-time flag for a tile loop's iteration: true for the check-free
+// iteration (the caller has shown that every per-tile test passes).
+template <bool B>
+struct LoopTag {
+    static constexpr bool value = B;
+};
+
 // s_waitcnt for "at most N vector-memory operations outstanding" (other
 // counters untouched).
 template <int N>
