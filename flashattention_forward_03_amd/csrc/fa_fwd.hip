@@ -200,7 +200,7 @@ __device__ __forceinline__ void attend_qtile(
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
             float alpha;
-            if (softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha))
+            if (__builtin_expect(softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha), 0))
                 rescale_acc<D>(oacc, alpha);
             // keep the V operand reads after the softmax (register pressure)
             __builtin_amdgcn_sched_barrier(0);
