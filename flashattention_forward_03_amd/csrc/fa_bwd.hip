@@ -119,10 +119,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         lim = min(lim, qrow + dq + 1);
 
     const u32x4s_t krs = make_rsrc(Kb, Nk * G::ROWB), vrs = make_rsrc(Vb, Nk * G::ROWB);
-    unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE], kstep[G::PIECES_PER_WAVE],
-        vstep[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, koff, kstep);   // both tiles are read by rows
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, voff, vstep);
+    unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, koff);   // both tiles are read by rows
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, voff);
     // copies of the next tile (in order) into ring slot st: resources at the
     // tile's first key, advanced by one tile per copy in scalar registers
     uint64_t kb_next = ((uint64_t)krs[1] << 32) | krs[0];
@@ -344,8 +343,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // resources sit at the next pair's first row and advance by one tile per
     // copy in scalar registers (re-based when the head changes), so the lane
     // offsets are the tile-0 ones and no division runs per tile.
-    unsigned qoff[G::PIECES_PER_WAVE], qstep[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff, qstep);   // Q and dO tiles: same row layout
+    unsigned qoff[G::PIECES_PER_WAVE];
+    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff);   // Q and dO tiles: same row layout
     const unsigned roff = lane < 32 ? (unsigned)lane * 4u : kOutOfRange;
     uint32_t qlds[STAGES], glds[STAGES], llds[STAGES], dlds[STAGES];
 #pragma unroll

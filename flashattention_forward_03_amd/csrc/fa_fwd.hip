@@ -117,9 +117,8 @@ __device__ __forceinline__ void attend_qtile(
     qk_offsets<D>(sigma(l32), hh, ko);
     const u32x4s_t krsrc = make_rsrc(Kb, Nk * krs), vrsrc = make_rsrc(Vb, Nk * vrs);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
-    unsigned kstep[G::PIECES_PER_WAVE], vstep[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, d, krs, koff, kstep);
-    dma_offsets<D, false>(wave, lane, d, vrs, voff, vstep);
+    dma_offsets<D, true>(wave, lane, d, krs, koff);
+    dma_offsets<D, false>(wave, lane, d, vrs, voff);
 
     // Copies of the next tile into ring slot `slot` (tiles are copied in
     // order): buffer resources at the tile's first key, advanced by one tile

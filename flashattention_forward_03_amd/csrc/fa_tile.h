@@ -70,20 +70,19 @@ struct Geometry {
     static_assert(PIECES_PER_WAVE * 4 == PIECES, "tile must split over 4 waves");
 };
 
-// Copy key rows [kt0, kt0 + BN) of one (b, h) into an LDS tile with the
-// buffer-to-LDS load (16 bytes per lane).  The buffer resource covers the
-// Nk rows of this (b, h) (row stride rs bytes); rows past Nk are out of
-// range and read as zero (those keys are always masked).  off[u] is the
-// lane's byte offset for its u-th 1 KB piece of tile 0 (chunk picked so
-// that it lands in its swizzled LDS slot); step[u] is what one tile row
-// adds to it: 0 for the padding columns past d, whose offset lies beyond
-// any buffer range so that they read as zero.
+// A tile of BN rows is copied into LDS with the buffer-to-LDS load (16
+// bytes per lane) from a buffer resource whose base is the tile's first row
+// (row stride rs bytes) and whose range ends at the last valid row: rows
+// past it read as zero (those keys or rows are always masked).  off[u] is
+// the lane's byte offset for its u-th 1 KB piece of the tile (chunk picked
+// so that it lands in its swizzled LDS slot), the same for every tile; the
+// padding columns past d get an offset beyond any buffer range, so they
+// read as zero too.
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any buffer range (< 2^31 bytes)
 
 template <int D, bool IS_K>
 __device__ __forceinline__ void dma_offsets(int wave, int lane, int d, unsigned rs,
-                                            unsigned (&off)[Geometry<D>::PIECES_PER_WAVE],
-                                            unsigned (&step)[Geometry<D>::PIECES_PER_WAVE])
+                                            unsigned (&off)[Geometry<D>::PIECES_PER_WAVE])
 {
     using G = Geometry<D>;
 #pragma unroll
@@ -94,7 +93,6 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, int d, unsigned 
         const int lc = swz_slot<G::DC>(pc, IS_K ? swz_k(row) : swz_v(row));
         const bool valid = lc * 8 < d;
         off[u] = valid ? (unsigned)row * rs + (unsigned)lc * 16u : kOutOfRange;
-        step[u] = valid ? rs : 0u;
     }
 }
 
@@ -117,31 +115,6 @@ __device__ __forceinline__ u32x4s_t make_rsrc(const void *base, int nbytes)
     r[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
     r[3] = 0x00020000u;
     return r;
-}
-
-// The per-tile step is either kept per lane (step[]) or derived from the
-// out-of-range sentinel (rs): the second costs two VALU per copy and saves
-// the step registers, which lets d = 32 run 4 waves per SIMD and d = 128
-// spill less (measured faster there, slower at d = 64).
-template <int D>
-__device__ __forceinline__ void dma_tile(const u32x4s_t &rsrc, const unsigned *off, const unsigned *step, unsigned rs,
-                                         int kt0, unsigned char *dst, int wave)
-{
-    using G = Geometry<D>;
-#pragma unroll
-    for (int u = 0; u < G::PIECES_PER_WAVE; ++u) {
-        const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(lds_void *)(dst + (u * 4 + wave) * 1024));
-        uint32_t voff;
-        if constexpr (D == 64)
-            voff = off[u] + (unsigned)kt0 * step[u];
-        else
-            voff = off[u] == kOutOfRange ? kOutOfRange : off[u] + (unsigned)kt0 * rs;
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                     :
-                     : "v"(voff), "s"(lds_addr), "s"(rsrc)
-                     : "memory", "m0");
-    }
 }
 
 // The same copy from a buffer resource that starts at the tile's first row:
