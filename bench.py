@@ -97,7 +97,7 @@ def kernel_digest(sources=FWD_SOURCES):
     return h.hexdigest()[:16]
 
 
-DEC_SOURCES = ("fa_decode.hip", "fa_common.h")
+DEC_SOURCES = ("fa_decode.hip", "fa_tile.h", "fa_common.h")
 
 
 def measured_traffic(path=TRAFFIC_FILE, sources=FWD_SOURCES):
