@@ -69,6 +69,23 @@ def test_backward_parity(B, H, Hkv, Nq, Nk, dtype, causal, lens):
                                     f"lens={lens}")
 
 
+@pytest.mark.parametrize("H,Hkv,Nq,Nk,causal", [
+    (2, 2, 33, 33, True),
+    (2, 2, 134, 97, True),     # more query rows than keys: rows past the diagonal
+    (2, 2, 97, 161, False),
+    (4, 1, 161, 161, True),    # four query heads per K/V head: the dK/dV pass walks 4 heads
+    (4, 2, 70, 97, False),
+    (3, 1, 96, 64, True),
+])
+def test_backward_tile_boundaries(H, Hkv, Nq, Nk, causal):
+    """Key and query counts around whole 32-row tiles, with groups of query
+    heads, for the passes' unchecked and checked iterations and for the
+    (query head, query tile) counters of the dK/dV pass."""
+    w = gen.fwd_inputs(1, H, Nq, Nk, 64, "bf16", seed=11900 + H * 10 + Nq + Nk, causal=causal,
+                       Hkv=Hkv)
+    _check(w, _dout(w, 11950 + Nq + Nk), f"bwd H{H}/{Hkv} Nq{Nq} Nk{Nk} causal={causal}")
+
+
 def test_backward_constant_v():
     """Equal V rows: O is that row everywhere, dS = 0, so dQ = dK = 0."""
     w = gen.fwd_inputs(1, 2, 150, 150, 64, "bf16", seed=11600, causal=True)

@@ -80,6 +80,20 @@ def test_ragged_shapes(B, H, Nq, Nk, d, dtype, causal, lens):
     full_parity(w, f"B{B} H{H} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} lens={lens}")
 
 
+@pytest.mark.parametrize("Nk", [32, 33, 64, 96, 97, 128, 161])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("extra_q", [0, 37])
+def test_tile_count_boundaries(Nk, causal, extra_q):
+    """Key counts around whole tiles: the kernel runs its unchecked iterations
+    for the tiles below min(tiles - 2, the wave's tiles, the first masked
+    tile) and checked ones after, so these counts put that split at every
+    phase of the three-slot ring; extra query rows move the causal diagonal."""
+    Nq = Nk + extra_q
+    w = gen.fwd_inputs(1, 2, Nq, Nk, 64, "bf16", seed=9100 + Nk + 7 * extra_q + causal,
+                       causal=causal, scale=0.125)
+    full_parity(w, f"Nq{Nq} Nk{Nk} causal={causal}")
+
+
 def test_zero_keys_gives_zero_output_and_minus_inf_lse():
     import torch
 
