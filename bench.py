@@ -90,10 +90,15 @@ FWD_SOURCES = ("fa_fwd.hip", "fa_tile.h", "fa_common.h")
 
 
 def kernel_digest(sources=FWD_SOURCES):
+    """Digest of the kernel sources and of the flags the first one (the
+    kernel's own file) is compiled with."""
+    from flashattention_forward_03_amd import build as fa_build
+
     h = hashlib.sha256()
     for name in sources:
         with open(os.path.join(ROOT, "flashattention_forward_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(fa_build.flags_for(sources[0])).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
 
 
