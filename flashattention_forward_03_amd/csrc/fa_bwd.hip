@@ -118,7 +118,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     if (causal)
         lim = min(lim, qrow + dq + 1);
 
-    const u32x4s_t krs = make_rsrc(Kb, Nk * G::ROWB), vrs = make_rsrc(Vb, Nk * G::ROWB);
+    // ranges end at the last valid key: padded rows [kvlen, Nk) read as zero,
+    // so their (masked) products add 0 * 0, never 0 * NaN from caller memory
+    const u32x4s_t krs = make_rsrc(Kb, kvlen * G::ROWB), vrs = make_rsrc(Vb, kvlen * G::ROWB);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
     dma_offsets<D, true>(wave, lane, D, G::ROWB, koff);   // both tiles are read by rows
     dma_offsets<D, true>(wave, lane, D, G::ROWB, voff);
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // K and V rows of this lane's key (B operands)
     u32x4_t kf[G::KSTEPS], vf[G::KSTEPS];
     {
-        const bool ok = key < Nk;
+        const bool ok = key < kvlen;   // padded keys: zero operands (their P and dS are masked)
         const size_t r = ((size_t)g * Nk + (ok ? key : 0)) * D + 8 * hh;
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {

@@ -17,7 +17,7 @@
 //   * key tiles of 32 rows at d = 64 / 128, 64 at d = 32 / 96.  K and V tiles
 //     are copied HBM/L2 -> LDS by the buffer-to-LDS load (16 bytes per lane,
 //     no VGPR staging); each lane fetches the chunk that belongs at its
-//     XOR-swizzled LDS slot, and rows past Nk (and columns past d) fall
+//     XOR-swizzled LDS slot, and rows past the valid keys (and columns past d) fall
 //     outside the buffer range and read as zero.  The LDS ring holds three K
 //     and three V tiles (two at d = 128), filled two tiles ahead of use;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA so
@@ -115,7 +115,12 @@ __device__ __forceinline__ void attend_qtile(
     const float tau_log2 = kRescaleLog2<BF16>;
     int ko[G::NBLK][G::KSTEPS];   // K operand read offsets inside a tile
     qk_offsets<D>(sigma(l32), hh, ko);
-    const u32x4s_t krsrc = make_rsrc(Kb, Nk * krs), vrsrc = make_rsrc(Vb, Nk * vrs);
+    // The K/V ranges end at the last valid key (kvlen), not at Nk: rows
+    // [kvlen, Nk) are masked, but the P V product would still multiply their
+    // zero probabilities by whatever the caller left there (0 * NaN = NaN),
+    // so they must read as zero.  The issued tiles all start below kvlen, so
+    // the range moved per copy stays positive.
+    const u32x4s_t krsrc = make_rsrc(Kb, kvlen * krs), vrsrc = make_rsrc(Vb, kvlen * vrs);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
     dma_offsets<D, true>(wave, lane, d, krs, koff);
     dma_offsets<D, false>(wave, lane, d, vrs, voff);
@@ -123,7 +128,7 @@ __device__ __forceinline__ void attend_qtile(
     // Copies of the next tile into ring slot `slot` (tiles are copied in
     // order): buffer resources at the tile's first key, advanced by one tile
     // per copy in scalar registers, so the lane offsets stay those of tile 0
-    // (keys past Nk are out of range); ring slots as 32-bit LDS addresses.
+    // (keys past kvlen are out of range); ring slots as 32-bit LDS addresses.
     uint64_t kb_next = ((uint64_t)krsrc[1] << 32) | krsrc[0];
     uint64_t vb_next = ((uint64_t)vrsrc[1] << 32) | vrsrc[0];
     uint32_t kr_next = krsrc[2], vr_next = vrsrc[2];

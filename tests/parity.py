@@ -2,6 +2,8 @@
 binding, compare with the fp64 oracle at the stated tolerances."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import fa_inputs as gen
@@ -41,6 +43,12 @@ def compare(o, lse, o_ref, lse_ref, what="", out_dtype="f32"):
     assert mean_abs <= TOL_MEAN, f"{what}: mean abs {mean_abs:.3e} {stats}"
     assert lse_rel <= TOL_LSE, f"{what}: lse {lse_rel:.3e} {stats}"
     return stats
+
+
+def host_cores(cap=16):
+    """Threads for the oracle at full size: the cores this process may run on,
+    at most `cap` (a GPU machine shares its host between its GPUs)."""
+    return max(1, min(cap, len(os.sched_getaffinity(0))))
 
 
 def device_tensors(w: gen.FwdInputs, device="cuda"):

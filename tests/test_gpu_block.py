@@ -14,11 +14,15 @@ roundoff of the 16-bit dtype; e = 2^-24 for fp32):
     |res|), one rounding u |y|;
   * the block's Q/K/V stage against the folded oracle (the same stored
     gamma W as the library's fold): the fp32 terms and the rounding of y only;
-  * the block's attention stage: the attention bar (max 1e-2, mean 1e-3 on O,
-    1e-3 max(1, |LSE|)) plus half an ulp of the 16-bit O, against the folded
-    oracle's attention on its own rounded qkv; the block output: that O bar
-    carried through W_o (1e-2 |W_o| row sums, mean 1e-3) plus the dense-layer
-    bar.
+  * the block's attention stage against the plain definition: the attention
+    bar (max 1e-2, mean 1e-3 on O, 1e-3 max(1, |LSE|)) plus half an ulp of the
+    16-bit O, each element's bar widened by the exact effect of the library's
+    one rounding that the definition lacks (gamma W stored in the dtype): the
+    oracle evaluates the block in both forms and takes the difference.  The
+    folded form is also checked at the plain attention bar;
+  * the block output against the definition: the O bar carried through W_o
+    (1e-2 |W_o| row sums, mean 1e-3), the dense-layer bar and the same
+    fold effect on y.
 """
 import math
 
@@ -28,7 +32,7 @@ import pytest
 import fa_inputs as gen
 import oracle
 from oracle import block as ob
-from parity import compare
+from parity import compare, host_cores
 
 pytestmark = pytest.mark.gpu
 
@@ -256,33 +260,66 @@ def check_block(w, y, views, ref, tokens=None):
     wf, bf = ob.fold_weights(w.gamma, w.beta, w.w_qkv, w.b_qkv, dt)
     y_f, raw_f = ob.ln_linear_folded(xs, dt, wf, bf, w.eps)
     _check("block qkv (folded)", qkv, y_f, folded_bound(w, xs, dt, y_f, raw_f))
-    # stage 2: attention (bar of the forward, 16-bit O) on the folded oracle's qkv
+    # stage 2: attention, held to the plain definition.  The library's one
+    # deviation from it is the 16-bit rounding of gamma W (the fold); its
+    # effect on O and LSE is evaluated exactly by the oracle (the same block in
+    # both forms, both in fp64 from the inputs) and widens the forward's bar
+    # element by element.  The folded form is a secondary check at the
+    # forward's own bar.
     o = _host(pick(views["o"]), dt)
     lse_all = _host(views["lse"], dt)
     H = w.H
     if tokens is None:
         lse = lse_all.transpose(0, 2, 1).reshape(w.T, H)
-        lse_ref = ref["lse"].transpose(0, 2, 1).reshape(w.T, H)
+        to_rows = lambda a: a.transpose(0, 2, 1).reshape(w.T, H)
     else:
         b, n = tokens // w.N, tokens % w.N
         lse = lse_all[b, :, n]
-        lse_ref = ref["lse"]
-    compare(o.reshape(-1, w.d), lse.reshape(-1), ref["o"].reshape(-1, w.d), lse_ref.reshape(-1),
-            "block attention", out_dtype=dt)
-    # stage 3: output layer + residual, with the O bar carried through W_o
+        to_rows = lambda a: a
+    p, f = ref["plain"], ref["folded"]
+    lse_p, lse_f = to_rows(p["lse"]), to_rows(f["lse"])
+    fold_o = np.abs(f["o"] - p["o"])
+    fold_lse = np.abs(lse_f - lse_p)
+    o_err = np.maximum(np.abs(o - p["o"]) - _u(dt) / 2 * np.abs(p["o"]) - fold_o, 0.0)
+    fin = np.isfinite(lse_p)
+    assert np.array_equal(np.isfinite(lse), fin), "block attention: -inf LSE rows differ"
+    lse_err = np.maximum(np.abs(lse[fin] - lse_p[fin]) - fold_lse[fin], 0.0) / \
+        np.maximum(1.0, np.abs(lse_p[fin]))
+    raw = dict(max_abs=float(np.abs(o - p["o"]).max()), mean_abs=float(np.abs(o - p["o"]).mean()),
+               lse_rel=float((np.abs(lse[fin] - lse_p[fin]) / np.maximum(1.0, np.abs(lse_p[fin]))).max()),
+               fold_o_max=float(fold_o.max()), fold_lse_max=float(fold_lse[fin].max(initial=0.0)))
+    print("block attention vs the definition", raw, flush=True)
+    assert np.all(np.isfinite(o)), "block attention: non-finite O"
+    assert o_err.max() <= 1e-2 and o_err.mean() <= 1e-3 and lse_err.max(initial=0.0) <= 1e-3, \
+        ("block attention vs the definition", float(o_err.max()), float(o_err.mean()),
+         float(lse_err.max(initial=0.0)))
+    compare(o.reshape(-1, w.d), lse.reshape(-1), f["o"].reshape(-1, w.d), lse_f.reshape(-1),
+            "block attention (folded form)", out_dtype=dt)
+    # stage 3: output layer + residual against the definition: the O bar
+    # carried through W_o, the dense-layer bar, and the fold's effect on y
     Wo = np.abs(gen.bits_to_float(w.w_o, dt).astype(np.float64))
     x = np.abs(gen.bits_to_float(xs, dt).astype(np.float64))
     u = _u(dt)
-    carried = 1e-2 * Wo.sum(axis=1)[None, :] + u * ref["oprod"]
-    bound = carried + (1 + 1e-3) * u * np.abs(ref["y"]) + \
-        2 * (w.C + 4) * E32 * (ref["oprod"] + np.abs(w.b_o)[None, :] + x) + 1e-7
+    fold_y = np.abs(f["y"] - p["y"])
+    carried = 1e-2 * Wo.sum(axis=1)[None, :] + u * p["oprod"]
+    bound = carried + (1 + 1e-3) * u * np.abs(p["y"]) + \
+        2 * (w.C + 4) * E32 * (p["oprod"] + np.abs(w.b_o)[None, :] + x) + fold_y + 1e-7
     got = _host(pick(y), dt)
-    _check("block y", got, ref["y"], bound)
-    mean_bar = float((1e-3 * Wo.sum(axis=1)).mean() + u * np.abs(ref["y"]).mean()
-                     + u * ref["oprod"].mean())
-    err = float(np.abs(got - ref["y"]).mean())
-    print(f"block y mean|d|={err:.3e} bar={mean_bar:.3e}", flush=True)
+    _check("block y (definition)", got, p["y"], bound)
+    mean_bar = float((1e-3 * Wo.sum(axis=1)).mean() + u * np.abs(p["y"]).mean()
+                     + u * p["oprod"].mean() + fold_y.mean())
+    err = float(np.abs(got - p["y"]).mean())
+    print(f"block y mean|d|={err:.3e} bar={mean_bar:.3e} (fold effect {fold_y.mean():.3e})", flush=True)
     assert err <= mean_bar
+
+
+def block_refs(w, tokens=None, nthreads=0):
+    """The oracle's block in its plain form (the definition) and in its folded
+    form (gamma W stored in the dtype)."""
+    args = (w.x, w.dtype, w.gamma, w.beta, w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.B, w.N, w.H, w.Hkv,
+            w.d, w.eps, w.scale, w.causal, w.kv_lens)
+    return {"plain": ob.prenorm_attention(*args, tokens=tokens, nthreads=nthreads, folded=False),
+            "folded": ob.prenorm_attention(*args, tokens=tokens, nthreads=nthreads, folded=True)}
 
 
 @pytest.mark.parametrize("B,N,H,Hkv,d,dtype,causal,lens", [
@@ -295,9 +332,7 @@ def test_block_parity(B, N, H, Hkv, d, dtype, causal, lens):
     w = gen.block_inputs(B, N, H, d, dtype, 9300 + B * 100 + H * 10 + Hkv, Hkv=Hkv, causal=causal,
                          kv_len_range=lens)
     y, views, _ = run_block(w)
-    ref = ob.prenorm_attention(w.x, dtype, w.gamma, w.beta, w.w_qkv, w.b_qkv, w.w_o, w.b_o, B, N, H,
-                               Hkv, d, w.eps, w.scale, causal, w.kv_lens, folded=True)
-    check_block(w, y, views, ref)
+    check_block(w, y, views, block_refs(w))
 
 
 def test_block_equals_its_stages_bitwise():
@@ -335,7 +370,4 @@ def test_block_full_size_sampled():
     rng = np.random.default_rng(w.seed)
     tokens = np.sort(rng.choice(w.T, size=512, replace=False))
     tokens = np.concatenate([[0, w.N - 1, w.T - 1], tokens])
-    ref = ob.prenorm_attention(w.x, w.dtype, w.gamma, w.beta, w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.B,
-                               w.N, w.H, w.Hkv, w.d, w.eps, w.scale, w.causal, w.kv_lens,
-                               tokens=tokens, folded=True)
-    check_block(w, y, views, ref, tokens=tokens)
+    check_block(w, y, views, block_refs(w, tokens=tokens, nthreads=host_cores()), tokens=tokens)
