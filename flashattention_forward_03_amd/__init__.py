@@ -39,11 +39,13 @@ FA_ERR_WORKSPACE = 5
 FA_ERR_HIP = 6
 FA_ERR_ARG = 7
 FA_ERR_NOMEM = 8
+FA_ERR_SCRATCH = 9
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F32 = 2
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_bwd", "fa_decode_paged", "fa_decode_paged_gqa",
+            "fa_decode_paged_noalloc",
             "fa_kv_append", "fa_pager_create", "fa_pager_destroy", "fa_pager_reserve",
             "fa_pager_release", "fa_pager_length", "fa_pager_free_pages", "fa_pager_copy_table",
             "fa_decode_workspace_bytes", "fa_ln_stats", "fa_ln_fold_weights", "fa_ln_linear",
@@ -121,6 +123,8 @@ def load_library():
     lib.fa_decode_paged.restype = I
     lib.fa_decode_paged_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode_paged_gqa.restype = I
+    lib.fa_decode_paged_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.fa_decode_paged_noalloc.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_decode_workspace_bytes.restype = Z
     lib.fa_ln_stats.argtypes = [P, P, P, I, I, F, I, P]
@@ -230,6 +234,14 @@ def fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, 
                                               S, H, H_kv, d, page_size, max_pages_per_seq,
                                               num_pages, scale, dtype, workspace,
                                               workspace_bytes, stream)
+
+
+def fa_decode_paged_noalloc(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H_kv, d,
+                            page_size, max_pages_per_seq, num_pages, scale, dtype, stream) -> int:
+    return load_library().fa_decode_paged_noalloc(q, k_pages, v_pages, page_table, kv_lens, o,
+                                                  lse, S, H, H_kv, d, page_size,
+                                                  max_pages_per_seq, num_pages, scale, dtype,
+                                                  stream)
 
 
 def fa_decode_workspace_bytes(S, H, d, max_pages_per_seq, page_size) -> int:

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.h"
@@ -93,6 +94,7 @@ const char *fa_status_str(int status)
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, page size or dtype";
     case FA_ERR_ALIGN: return "pointer not aligned as required";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_SCRATCH: return "problem needs more scratch than the no-allocation entry point's fixed buffer";
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0; causal 0 or 1; eps finite and >= 0)";
     case FA_ERR_NOMEM: return "not enough free pages";
@@ -246,10 +248,54 @@ size_t fa_decode_workspace_bytes(int S, int H, int d, int max_pages_per_seq, int
     return decode_ws_bytes(S, H, d, max_pages_per_seq);
 }
 
-int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
-                        const int32_t *kv_lens, float *o, float *lse, int S, int H, int H_kv, int d, int page_size,
-                        int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
-                        size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Fixed device scratch of the no-allocation decode entry point: the split-KV
+// partials live here instead of in a caller workspace.  Every GPU the library
+// runs on holds one copy until the process ends.  Host code never names the
+// array directly (in host code the name is a stand-in, not a device address):
+// it uses the address that hipGetSymbolAddress returned for the current
+// device.
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device (set once)
+
+// The scratch address on the current device: looked up on the first call
+// per device (with that device current), cached afterwards.
+hipError_t scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Paged decode behind fa_decode_paged{,_gqa,_noalloc}: argument checks, then
+// the split-KV partials in the caller's workspace or (use_scratch) in the
+// library's fixed device scratch.
+int decode_impl(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                const int32_t *kv_lens, float *o, float *lse, int S, int H, int H_kv, int d, int page_size,
+                int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
+                size_t workspace_bytes, bool use_scratch, void *stream)
 {
     if (S < 0 || H < 0 || max_pages_per_seq < 1 || num_pages < 1)
         return FA_ERR_SHAPE;
@@ -275,11 +321,19 @@ int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages,
         !aligned(page_table, 4) || !aligned(kv_lens, 4) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
     const size_t need = decode_ws_bytes(S, H, d, max_pages_per_seq);
-    if (need > 0) {
+    if (use_scratch) {
+        if (need > kNoAllocScratchBytes)
+            return FA_ERR_SCRATCH;
+    } else if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return FA_ERR_WORKSPACE;
         if (!aligned(workspace, 16))
             return FA_ERR_ALIGN;
+    }
+    if (use_scratch && need > 0) {
+        const hipError_t e = scratch_on_current_device(&workspace);
+        if (e != hipSuccess)
+            return hip_fail(e, "fa_decode_paged_noalloc scratch lookup");
     }
     const long long chunks = fa::decode_max_chunks(max_pages_per_seq);
     float *part_o = need ? static_cast<float *>(workspace) : nullptr;
@@ -293,6 +347,19 @@ int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages,
     return FA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                        const int32_t *kv_lens, float *o, float *lse, int S, int H, int H_kv, int d, int page_size,
+                        int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    return decode_impl(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H_kv, d, page_size,
+                       max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes, false, stream);
+}
+
 int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
                     const int32_t *kv_lens, float *o, float *lse, int S, int H, int d, int page_size,
                     int max_pages_per_seq, int num_pages, float scale, int dtype, void *workspace,
@@ -300,6 +367,15 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
 {
     return fa_decode_paged_gqa(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H, d, page_size,
                                max_pages_per_seq, num_pages, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_pages, const int32_t *page_table,
+                            const int32_t *kv_lens, float *o, float *lse, int S, int H, int H_kv, int d,
+                            int page_size, int max_pages_per_seq, int num_pages, float scale, int dtype,
+                            void *stream)
+{
+    return decode_impl(q, k_pages, v_pages, page_table, kv_lens, o, lse, S, H, H_kv, d, page_size,
+                       max_pages_per_seq, num_pages, scale, dtype, nullptr, 0, true, stream);
 }
 
 // ------------------------------------------------------ pre-LN block ---

@@ -69,6 +69,7 @@ extern "C" {
 #define FA_ERR_HIP 6         /* a HIP launch failed; see fa_last_hip_error() */
 #define FA_ERR_ARG 7         /* scale not finite and > 0, causal not 0/1, or eps not finite and >= 0 */
 #define FA_ERR_NOMEM 8       /* the page allocator has too few free pages */
+#define FA_ERR_SCRATCH 9     /* fa_decode_paged_noalloc: the problem needs more than its fixed scratch */
 
 /* element types of Q, K, V (and the KV pools); FA_DTYPE_F32 only for fa_fwd_ex's O */
 #define FA_DTYPE_F16 0
@@ -228,6 +229,33 @@ int fa_decode_paged_gqa(const void *q, const void *k_pages, const void *v_pages,
                         int S, int H, int H_kv, int d, int page_size, int max_pages_per_seq,
                         int num_pages, float scale, int dtype, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * fa_decode_paged_gqa without a workspace argument, for callers that cannot
+ * allocate device memory at all (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The split-KV partials go to a
+ * fixed scratch array inside the library instead: 40 MiB (41943040 bytes) of
+ * device memory that every GPU the library runs on holds until the process
+ * ends.  The call itself allocates and frees nothing.
+ *
+ *   Every argument, layout, alignment and error as for fa_decode_paged_gqa;
+ *   the result is bitwise equal to that call's on the same inputs.
+ *   FA_ERR_SCRATCH when fa_decode_workspace_bytes(S, H, d, max_pages_per_seq,
+ *   page_size) exceeds 41943040 bytes (e.g. S = 32, H = 32, d = 128 fits with
+ *   up to 624 pages of 16 tokens per sequence), checked before any HIP call.
+ *
+ * All calls on one GPU share that GPU's scratch: calls that overlap in time on
+ * one GPU (other streams, other threads) race and give unspecified results;
+ * serialise them (e.g. one stream).  The scratch's contents on entry do not
+ * matter (nothing in it needs to start at zero).  The first call on each
+ * device looks up the scratch's device address (hipGetSymbolAddress) with
+ * that device current; a failure there is FA_ERR_HIP.
+ */
+int fa_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_pages,
+                            const int32_t *page_table, const int32_t *kv_lens, float *o,
+                            float *lse, int S, int H, int H_kv, int d, int page_size,
+                            int max_pages_per_seq, int num_pages, float scale, int dtype,
+                            void *stream);
 
 /*
  * Paged KV cache: append (inference kernel cookbook page, recipe 02 "KV Cache":

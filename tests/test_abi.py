@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert fa.load_library().fa_version() == 1
-    for code in range(0, 8):
+    for code in range(0, 10):
         s = fa.fa_status_str(code)
         assert s and s != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
@@ -199,6 +199,43 @@ def call_dec_gqa(H_kv, **over):
 ])
 def test_decode_gqa_argument_checks(lib, H, H_kv, over, status):
     assert call_dec_gqa(H_kv, H=H, **over) == status
+
+
+def call_noalloc(H_kv, **over):
+    a = dict(GOOD_DEC)
+    a.update(over)
+    return fa.fa_decode_paged_noalloc(a["q"], a["kp"], a["vp"], a["pt"], a["kl"], a["o"],
+                                      a["lse"], a["S"], a["H"], H_kv, a["d"], a["page_size"],
+                                      a["max_pages"], a["num_pages"], a["scale"], a["dtype"],
+                                      a["stream"])
+
+
+# the no-allocation decode: the same checks as fa_decode_paged_gqa, and a
+# problem whose split-KV partials exceed the fixed 40 MiB scratch is refused
+# before any HIP call (S32 H32 d128: 78 chunks of 8 pages fit, 79 do not)
+@pytest.mark.parametrize("H,H_kv,over,status", [
+    (8, 3, {}, fa.FA_ERR_SHAPE),
+    (8, 2, dict(S=-1), fa.FA_ERR_SHAPE),
+    (8, 2, dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (8, 2, dict(page_size=32), fa.FA_ERR_UNSUPPORTED),
+    (8, 2, dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (8, 2, dict(kp=None), fa.FA_ERR_NULL),
+    (8, 2, dict(o=A + 4), fa.FA_ERR_ALIGN),
+    (0, 0, dict(q=None, o=None), fa.FA_OK),
+    (32, 8, dict(S=32, max_pages=79 * 8), fa.FA_ERR_SCRATCH),
+    (32, 32, dict(S=32, max_pages=632), fa.FA_ERR_SCRATCH),
+    (8, 2, dict(S=1 << 14, max_pages=512), fa.FA_ERR_SCRATCH),
+])
+def test_decode_noalloc_argument_checks(lib, H, H_kv, over, status):
+    assert call_noalloc(H_kv, H=H, **over) == status
+
+
+def test_decode_noalloc_scratch_limit_matches_the_header(lib):
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert "41943040 bytes" in text
+    # largest S32 H32 d128 problem that fits: 624 pages per sequence
+    assert fa.fa_decode_workspace_bytes(32, 32, 128, 624, 16) <= 41943040
+    assert fa.fa_decode_workspace_bytes(32, 32, 128, 632, 16) > 41943040
 
 
 def test_binding_checks_head_grouping(lib):
