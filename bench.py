@@ -12,13 +12,20 @@ already resident in HBM:
     8 K/V heads (grouped-query attention).
 Each kernel is bracketed by HIP events on the stream it is launched on.
 
-Prints ONE JSON line.  ``value`` is forward TFLOP/s (nominal FLOPs
-4*B*H*Nq*Nk*d, halved for causal, over the forward's average event time);
+Prints ONE JSON line.  ``value`` is forward TFLOP/s: nominal FLOPs
+4*B*H*Nq*Nk*d, halved for causal, over the forward's median launch time in
+the timed steps (HIP events); ``fwd`` also gives p10 / p90 / mean.
 ``roofline`` is the forward kernel against the dense bf16 MFMA peak;
 ``decode`` and ``decode_gqa`` carry the decode GB/s against the 8 TB/s HBM
-peak; and
-``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-forward workload on the host cores (and reports the sample's parity).
+peak.
+``configs`` times every configuration of the workloads one by one (20 warmup
++ 200 launches each by default, median / p10 / p90): the f16 B1 H1 N256 and
+N2048 forwards, the causal B8 H16 d64 sweep N = 512 / 1024 / 2048 / 4096, the
+padded B8 H16 N2048 encoder shape (nominal and effective FLOPs) and the
+decode batch; beside each, the fp64 oracle's wall time on the host cores
+(one thread too for the B1 H1 configs and the decode) and the parity of the
+GPU output over every element.  ``cpu_baseline`` is the oracle on the
+headline workload (every row, all host cores up to 16).
 ``backward`` times fa_bwd (D pass, dK/dV pass, dQ pass) on the headline
 shape outside the step: nominal FLOPs 2.5x the forward's (five products of
 the forward's size against two).
@@ -28,6 +35,7 @@ on the bytes read plus written.
 ``variants`` times generalised forward launches outside the step (head dims
 32 / 96 / 128, [B, N, H, d] inputs with a bf16 O, 4 K/V heads) on the same
 causal B8 H16 N4096 shape, each against the bf16 MFMA peak.
+All the timings outside the step use the same protocol as ``configs``.
 """
 from __future__ import annotations
 
@@ -84,6 +92,46 @@ def decode_bytes(kv_lens, H, d, elem=2, with_io=True, Hkv=None):
 def fwd_bytes(B, H, Nq, Nk, d, elem=2):
     """Compulsory HBM bytes of the forward: Q, K, V once, O (fp32) and LSE once."""
     return B * H * (Nq + 2 * Nk) * d * elem + B * H * Nq * d * 4 + B * H * Nq * 4
+
+
+def effective_flops(B, H, Nq, Nk, d, causal, kv_lens=None):
+    """FLOPs over the (row, key) pairs the mask leaves valid: 4*d per pair.
+    For key padding: 4*H*d*Nq*sum_b kv_len_b (non-causal); for causal, each
+    row i counts min(i+1+Nk-Nq, kv_len) keys."""
+    lens = np.full(B, Nk, np.int64) if kv_lens is None else np.asarray(kv_lens, np.int64)
+    if not causal:
+        return 4.0 * H * d * Nq * float(lens.sum())
+    i = np.arange(Nq, dtype=np.int64)
+    tot = 0
+    for n in lens:
+        tot += int(np.clip(np.minimum(i + 1 + Nk - Nq, n), 0, None).sum())
+    return 4.0 * H * d * float(tot)
+
+
+def launch_stats(ms):
+    """Median, p10, p90 and mean of per-launch times (ms)."""
+    ms = np.asarray(ms, np.float64)
+    return {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "mean_ms": float(ms.mean()),
+            "launches": int(ms.size)}
+
+
+def event_times(fn, warmup, launches):
+    """Per-launch times (ms) of fn() over `launches` launches after `warmup`
+    untimed ones: each launch bracketed by HIP events on the current stream
+    (the stream the library launches on)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
 
 
 FWD_SOURCES = ("fa_fwd.hip", "fa_tile.h", "fa_common.h")
@@ -166,58 +214,110 @@ def record_traffic(d, copy_bytes):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(w, o_gpu, lse_gpu, target_s, seed=12345):
-    """Time the fp64 oracle on a bounded sample of query rows of the forward
-    workload (uniformly drawn rows, so the sample has the workload's mix of
-    causal row lengths).  Returns the baseline dict."""
+# The pages' workload configurations: name -> config number.  Config 3 is the
+# causal sweep (the headline is its N = 4096 point); config 5 is the decode.
+FWD_CONFIGS = (
+    ("fwd_b1h1_n256_d64_f16", "1"),
+    ("fwd_b1h1_n2048_d64_f16", "2"),
+    ("fwd_causal_b8h16_n512_d64_bf16", "3"),
+    ("fwd_causal_b8h16_n1024_d64_bf16", "3"),
+    ("fwd_causal_b8h16_n2048_d64_bf16", "3"),
+    (FWD_WORKLOAD, "3"),
+    ("fwd_padded_b8h16_n2048_d64_bf16", "4"),
+)
+SINGLE_THREAD_CONFIGS = ("1", "2", "5")
+
+
+def _parity(o, lse, o_ref, lse_ref):
+    """max / mean |dO| and max |dLSE| / max(1, |LSE|) over every element."""
+    err = np.abs(np.asarray(o, np.float64) - o_ref)
+    fin = np.isfinite(lse_ref)
+    lse = np.asarray(lse, np.float64)
+    lrel = np.abs(lse[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+    return {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()),
+            "lse_rel": float(lrel.max(initial=0.0))}
+
+
+def time_fwd_configs(fa, dev, warmup, launches, with_oracle, cores, headline=None):
+    """Every forward configuration: GPU time per launch (median, p10, p90 over
+    `launches` after `warmup`, HIP events), nominal TFLOP/s (and effective
+    TFLOP/s over the unmasked pairs), and, with_oracle, the fp64 oracle's wall
+    time on all `cores` (single-threaded too for configs 1 and 2) with the
+    parity of the GPU output over every element.  ``headline``: the headline
+    workload's (inputs, device tensors) to reuse."""
+    import torch
+
+    out = {}
+    for name, cfg in FWD_CONFIGS:
+        print(f"[bench] config {cfg}: {name}", file=sys.stderr, flush=True)
+        if headline is not None and name == FWD_WORKLOAD:
+            w, (q, k, v) = headline
+        else:
+            w = gen.fwd_workload(name)
+            q, k, v = (gen.to_torch(x, w.dtype).to(dev) for x in (w.q, w.k, w.v))
+        B, H, Nq, Nk, d = w.shape
+        kl = None if w.kv_lens is None else torch.from_numpy(w.kv_lens).to(dev)
+        o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        call = lambda: fa.forward(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl, out=(o, lse))
+        st = launch_stats(event_times(call, warmup, launches))
+        nom = attention_flops(B, H, Nq, Nk, d, w.causal)
+        eff = effective_flops(B, H, Nq, Nk, d, w.causal, w.kv_lens)
+        sec = st["median_ms"] / 1e3
+        rec = {"config": cfg, "shape": {"B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d},
+               "dtype": w.dtype, "causal": w.causal, "padded": w.kv_lens is not None,
+               "seed": w.seed, "gpu": st, "flops_nominal": nom, "flops_effective": eff,
+               "TFLOP/s": nom / sec / 1e12, "TFLOP/s_effective": eff / sec / 1e12,
+               "frac": nom / sec / 1e12 / PEAK_BF16_TFLOPS, "workgroups": (Nq + 127) // 128 * B * H}
+        if with_oracle:
+            import oracle
+
+            o_h, l_h = o.cpu().numpy(), lse.cpu().numpy()
+            t0 = time.perf_counter()
+            o_ref, l_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal,
+                                                w.kv_lens, nthreads=cores)
+            dt = time.perf_counter() - t0
+            rec["oracle"] = {"seconds": dt, "threads": cores, "TFLOP/s": eff / dt / 1e12,
+                             "rows": B * H * Nq}
+            if cfg in SINGLE_THREAD_CONFIGS:
+                t0 = time.perf_counter()
+                oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, w.kv_lens,
+                                     nthreads=1)
+                rec["oracle"]["seconds_1_thread"] = time.perf_counter() - t0
+            rec["parity"] = _parity(o_h, l_h, o_ref, l_ref)
+            del o_ref, l_ref
+        out[name] = rec
+        del o, lse
+        if headline is None or name != FWD_WORKLOAD:
+            del q, k, v
+    return out
+
+
+def oracle_decode_times(dec, o_gpu, lse_gpu, cores):
+    """The decode batch through the fp64 oracle (all cores, then one thread),
+    and the parity of the GPU output over every element."""
     import oracle
 
-    B, H, Nq, Nk, d = w.shape
-    cores = len(os.sched_getaffinity(0))
-    rng = np.random.default_rng(seed)
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.decode(dec.q, dec.k, dec.v, dec.seq_off, dec.dtype, dec.scale,
+                                 nthreads=cores)
+    dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.decode(dec.q, dec.k, dec.v, dec.seq_off, dec.dtype, dec.scale, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    flops = 4.0 * dec.q.shape[1] * dec.q.shape[2] * float(np.sum(dec.kv_lens))
+    return {"seconds": dt, "threads": cores, "seconds_1_thread": dt1, "TFLOP/s": flops / dt / 1e12,
+            "parity": _parity(o_gpu, lse_gpu, o_ref, l_ref)}
 
-    def run(nrows):
-        rows = np.unique(rng.integers(0, B * H * Nq, size=nrows))
-        t0 = time.perf_counter()
-        o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal,
-                                              w.kv_lens, rows=rows, nthreads=cores)
-        dt = time.perf_counter() - t0
-        i = rows % Nq
-        n_valid = np.minimum(i + 1, Nk) if w.causal else np.full(rows.shape, Nk)
-        flops = float(np.sum(4.0 * d * n_valid))
-        return rows, o_ref, lse_ref, dt, flops
 
-    rows, o_ref, lse_ref, dt, flops = run(256 * cores)
-    if dt < target_s:
-        want = int(len(rows) * target_s / max(dt, 1e-3))
-        if want >= B * H * Nq:
-            # the whole workload fits the time budget: every row, in order
-            rows = np.arange(B * H * Nq, dtype=np.int64)
-            t0 = time.perf_counter()
-            o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal,
-                                                  w.kv_lens, rows=rows, nthreads=cores)
-            dt = time.perf_counter() - t0
-            i = rows % Nq
-            n_valid = np.minimum(i + 1, Nk) if w.causal else np.full(rows.shape, Nk)
-            flops = float(np.sum(4.0 * d * n_valid))
-        else:
-            rows, o_ref, lse_ref, dt, flops = run(want)
-    og = o_gpu.reshape(-1, d)[rows].astype(np.float64)
-    lg = lse_gpu.reshape(-1)[rows].astype(np.float64)
-    err = np.abs(og - o_ref)
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": cores,
-        "kind": "oracle",
-        "sample": (f"all {B * H * Nq} query rows" if len(rows) == B * H * Nq else
-                   f"{len(rows)} uniformly drawn query rows of {B * H * Nq}")
-                  + f" ({FWD_WORKLOAD}), fp64, {dt:.1f} s",
-        "seconds": dt,
-        "sample_parity": {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
-                          "lse_rel": float(np.max(np.abs(lg - lse_ref) /
-                                                  np.maximum(1, np.abs(lse_ref))))},
-    }
+def cpu_baseline_from(rec):
+    """The bench's cpu_baseline: the oracle on the headline workload (every
+    row), from its config record."""
+    B, H, Nq = rec["shape"]["B"], rec["shape"]["H"], rec["shape"]["Nq"]
+    orc = rec["oracle"]
+    return {"value": orc["TFLOP/s"], "unit": "TFLOP/s", "cores": orc["threads"], "kind": "oracle",
+            "sample": f"all {B * H * Nq} query rows ({FWD_WORKLOAD}), fp64, {orc['seconds']:.1f} s",
+            "seconds": orc["seconds"], "sample_parity": rec["parity"]}
 
 
 # Generalised forward launches on the headline shape (causal B8 H16 N4096):
@@ -255,19 +355,11 @@ def time_variants(fa, dev, steps, warmup):
         o = o.transpose(1, 2) if bshd else o
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         scale = 1.0 / math.sqrt(d)
-        for _ in range(warmup):
-            fa.forward(q, k, v, scale=scale, causal=True, out=(o, lse))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record()
-            fa.forward(q, k, v, scale=scale, causal=True, out=(o, lse))
-            b.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        tf = attention_flops(B, H, N, N, d, True) / (ms / 1e3) / 1e12
-        out[name] = {"kernel_ms_avg": ms, "TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS,
-                     "d": d, "H_kv": hkv, "layout": "bshd" if bshd else "bhsd", "o_dtype": odt}
+        st = launch_stats(event_times(
+            lambda: fa.forward(q, k, v, scale=scale, causal=True, out=(o, lse)), warmup, steps))
+        tf = attention_flops(B, H, N, N, d, True) / (st["median_ms"] / 1e3) / 1e12
+        out[name] = dict(st, **{"TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS, "d": d, "H_kv": hkv,
+                                "layout": "bshd" if bshd else "bhsd", "o_dtype": odt})
         del q, k, v, o, lse
     return out
 
@@ -283,21 +375,12 @@ def time_append(fa, dev, gq, kp, vp, pt, steps, warmup):
     seq = torch.from_numpy(np.repeat(np.arange(gq.S, dtype=np.int32), gq.kv_lens)).to(dev)
     pos = torch.from_numpy(np.concatenate([np.arange(n, dtype=np.int32)
                                            for n in gq.kv_lens])).to(dev)
-    for _ in range(warmup):
-        fa.kv_append(kn, vn, seq, pos, kp, vp, pt)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record()
-        fa.kv_append(kn, vn, seq, pos, kp, vp, pt)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    st = launch_stats(event_times(lambda: fa.kv_append(kn, vn, seq, pos, kp, vp, pt), warmup, steps))
     T = int(gq.kv_lens.sum())
     nbytes = 2 * 2 * T * gq.Hkv * gq.d * 2 + 2 * T * 4 + T * 4   # K+V read and written; ids
-    gbs = nbytes / (ms / 1e3) / 1e9
-    return {"workload": GQA_WORKLOAD, "tokens": T, "kernel_ms_avg": ms, "bytes": nbytes,
-            "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    gbs = nbytes / (st["median_ms"] / 1e3) / 1e9
+    return dict(st, **{"workload": GQA_WORKLOAD, "tokens": T, "bytes": nbytes, "GB/s": gbs,
+                       "frac": gbs / PEAK_HBM_GBS})
 
 
 def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
@@ -313,20 +396,13 @@ def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
     fa.forward(q, k, v, scale=w.scale, causal=w.causal, out=(o, lse))
     outs = (torch.empty_like(o), torch.empty(k.shape, dtype=torch.float32, device=dev),
             torch.empty(v.shape, dtype=torch.float32, device=dev), torch.empty_like(lse))
-    for _ in range(warmup):
-        fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record()
-        fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    st = launch_stats(event_times(
+        lambda: fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs),
+        warmup, steps))
     flops = 2.5 * attention_flops(B, H, Nq, Nk, d, w.causal)
-    tf = flops / (ms / 1e3) / 1e12
-    return {"workload": FWD_WORKLOAD, "kernel_ms_avg": ms, "TFLOP/s": tf,
-            "frac": tf / PEAK_BF16_TFLOPS, "flops": flops}
+    tf = flops / (st["median_ms"] / 1e3) / 1e12
+    return dict(st, **{"workload": FWD_WORKLOAD, "TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                       "flops": flops})
 
 
 def time_decode_groups(fa, dev, steps, warmup):
@@ -349,20 +425,11 @@ def time_decode_groups(fa, dev, steps, warmup):
         o = torch.empty((w.S, w.H, w.d), dtype=torch.float32, device=dev)
         lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
         call = lambda: fa.decode_paged(q, kp, vp, pt, kl, scale=w.scale, workspace=ws, out=(o, lse))
-        for _ in range(warmup):
-            call()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record()
-            call()
-            b.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        st = launch_stats(event_times(call, warmup, steps))
         nb = decode_bytes(w.kv_lens, w.H, w.d, Hkv=hkv)
-        gbs = nb / (ms / 1e3) / 1e9
-        out[f"h32_kv{hkv}"] = {"H": w.H, "H_kv": hkv, "kernel_ms_avg": ms, "bytes": nb, "GB/s": gbs,
-                               "frac": gbs / PEAK_HBM_GBS, "tokens": int(w.kv_lens.sum())}
+        gbs = nb / (st["median_ms"] / 1e3) / 1e9
+        out[f"h32_kv{hkv}"] = dict(st, **{"H": w.H, "H_kv": hkv, "bytes": nb, "GB/s": gbs,
+                                          "frac": gbs / PEAK_HBM_GBS, "tokens": int(w.kv_lens.sum())})
         del kp, vp
     return out
 
@@ -406,16 +473,7 @@ def time_block(fa, dev, steps, warmup):
     }
     res = {}
     for name, fn in stages.items():
-        for _ in range(warmup):
-            fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        res[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[name] = launch_stats(event_times(fn, warmup, steps))["median_ms"]
     fl_qkv = 2.0 * T * C * R
     fl_out = 2.0 * T * C * C
     fl_att = attention_flops(B, H, N, N, d, w.causal)
@@ -438,7 +496,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target wall time of the oracle baseline sample (0 = skip)")
+                    help="0 skips the fp64 oracle timings (cpu_baseline and the per-config "
+                         "oracle wall times); any other value runs them")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration timings (and with them the oracle)")
+    ap.add_argument("--config-launches", type=int, default=200,
+                    help="timed launches per configuration")
+    ap.add_argument("--config-warmup", type=int, default=20,
+                    help="untimed launches before each configuration's timed ones")
     ap.add_argument("--no-decode", action="store_true", help="time the forward only")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode")
     ap.add_argument("--no-variants", action="store_true",
@@ -570,8 +635,10 @@ def main():
     elapsed = time.perf_counter() - t0
 
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    fwd_avg_s = float(fwd_ms.mean()) / 1e3
-    tflops = fflops / fwd_avg_s / 1e12
+    fwd_st = launch_stats(fwd_ms)
+    fwd_s = fwd_st["median_ms"] / 1e3
+    tflops = fflops / fwd_s / 1e12
+    cores = min(16, len(os.sched_getaffinity(0)))
     result = {
         "metric": "attention fwd TFLOP/s (causal B8 H16 d64 N4096) + % MFMA peak; decode GB/s",
         "value": tflops,
@@ -591,53 +658,68 @@ def main():
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic()},
-        "fwd": {"kernel_ms_avg": float(fwd_ms.mean()), "kernel_ms_p10": float(np.percentile(fwd_ms, 10)),
-                "kernel_ms_p90": float(np.percentile(fwd_ms, 90)), "flops": fflops,
-                "compulsory_bytes": fwd_bytes(B, H, Nq, Nk, d)},
+        "peak_basis": {"bf16_mfma_TFLOP/s": PEAK_BF16_TFLOPS,
+                       "derivation": "256 CUs x 4096 bf16 FLOP/clk/CU x 2.4 GHz (dense)",
+                       "hbm_GB/s": PEAK_HBM_GBS},
+        "fwd": dict(fwd_st, flops=fflops, compulsory_bytes=fwd_bytes(B, H, Nq, Nk, d),
+                    value_basis="median launch time over the timed steps"),
     }
     if dec is not None:
-        dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-        gbs = dbytes / (float(dec_ms.mean()) / 1e3) / 1e9
-        result["decode"] = {
-            "GB/s": gbs, "kernel_ms_avg": float(dec_ms.mean()),
-            "kernel_ms_p10": float(np.percentile(dec_ms, 10)),
-            "kernel_ms_p90": float(np.percentile(dec_ms, 90)),
-            "bytes": dbytes, "tokens": int(dec.kv_lens.sum()),
+        dec_st = launch_stats([e[1].elapsed_time(e[2]) for e in events])
+        gbs = dbytes / (dec_st["median_ms"] / 1e3) / 1e9
+        result["decode"] = dict(dec_st, **{
+            "GB/s": gbs, "bytes": dbytes, "tokens": int(dec.kv_lens.sum()),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
-                         "traffic": measured_traffic(DEC_TRAFFIC_FILE, DEC_SOURCES)},
-        }
+                         "traffic": measured_traffic(DEC_TRAFFIC_FILE, DEC_SOURCES)}})
     if gq is not None:
-        g_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-        g_gbs = gbytes / (float(g_ms.mean()) / 1e3) / 1e9
-        result["decode_gqa"] = {
-            "GB/s": g_gbs, "kernel_ms_avg": float(g_ms.mean()),
-            "kernel_ms_p10": float(np.percentile(g_ms, 10)),
-            "kernel_ms_p90": float(np.percentile(g_ms, 90)),
-            "bytes": gbytes, "tokens": int(gq.kv_lens.sum()), "H": gq.H, "H_kv": gq.Hkv,
+        g_st = launch_stats([e[2].elapsed_time(e[3]) for e in events])
+        g_gbs = gbytes / (g_st["median_ms"] / 1e3) / 1e9
+        result["decode_gqa"] = dict(g_st, **{
+            "GB/s": g_gbs, "bytes": gbytes, "tokens": int(gq.kv_lens.sum()), "H": gq.H,
+            "H_kv": gq.Hkv,
             "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": g_gbs / PEAK_HBM_GBS,
-                         "traffic": measured_traffic(GQA_TRAFFIC_FILE, DEC_SOURCES)},
-        }
+                         "traffic": measured_traffic(GQA_TRAFFIC_FILE, DEC_SOURCES)}})
+    with_oracle = args.cpu_seconds > 0
+    if not args.no_configs:
+        # every configuration of the pages' workloads, one by one (20 warmup +
+        # 200 launches each, median / p10 / p90), with the oracle timed beside
+        # each on the host cores
+        cfgs = time_fwd_configs(fa, dev, args.config_warmup, args.config_launches, with_oracle,
+                                cores, headline=(w, (q, k, v)))
+        if dec is not None:
+            call = lambda: fa.decode_paged(dq, kp, vp, dpt, dkl, scale=dec.scale, workspace=ws,
+                                           out=(do, dlse))
+            st = launch_stats(event_times(call, args.config_warmup, args.config_launches))
+            rec = {"config": "5", "gpu": st, "bytes": dbytes,
+                   "GB/s": dbytes / (st["median_ms"] / 1e3) / 1e9, "seed": dec.seed}
+            rec["frac"] = rec["GB/s"] / PEAK_HBM_GBS
+            if with_oracle:
+                print("[bench] config 5: oracle", file=sys.stderr, flush=True)
+                rec["oracle"] = oracle_decode_times(dec, do.cpu().numpy(), dlse.cpu().numpy(), cores)
+            cfgs[DEC_WORKLOAD] = rec
+        result["configs"] = cfgs
+        if with_oracle:
+            result["cpu_baseline"] = cpu_baseline_from(cfgs[FWD_WORKLOAD])
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
-        result["backward"] = time_backward(fa, dev, q, k, v, o, lse, w, args.steps, args.warmup)
+        result["backward"] = time_backward(fa, dev, q, k, v, o, lse, w, args.config_launches,
+                                           args.config_warmup)
     if gq is not None and not args.no_variants:
         print("[bench] decode with wider query-head groups", file=sys.stderr, flush=True)
-        result["decode_groups"] = time_decode_groups(fa, dev, args.steps, args.warmup)
+        result["decode_groups"] = time_decode_groups(fa, dev, args.config_launches,
+                                                     args.config_warmup)
     if gq is not None and not args.no_append:
         print("[bench] kv append", file=sys.stderr, flush=True)
-        result["kv_append"] = time_append(fa, dev, gq, g_kp, g_vp, g_pt, args.steps, args.warmup)
+        result["kv_append"] = time_append(fa, dev, gq, g_kp, g_vp, g_pt, args.config_launches,
+                                          args.config_warmup)
     if not args.no_variants:
         print("[bench] forward variants", file=sys.stderr, flush=True)
-        result["variants"] = time_variants(fa, dev, args.steps, args.warmup)
+        result["variants"] = time_variants(fa, dev, args.config_launches, args.config_warmup)
     if not args.no_block:
         print("[bench] pre-LayerNorm block", file=sys.stderr, flush=True)
-        result["prenorm_block"] = time_block(fa, dev, args.steps, args.warmup)
-    if args.cpu_seconds > 0:
-        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, o.cpu().numpy(), lse.cpu().numpy(),
-                                              args.cpu_seconds)
+        result["prenorm_block"] = time_block(fa, dev, args.config_launches, args.config_warmup)
     print(json.dumps(result), flush=True)
 
 

@@ -41,3 +41,26 @@ def test_more_than_one_gpu_is_refused():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True)
     assert out.returncode == 2 and "one GPU" in out.stderr
+
+
+def test_effective_flops_counts_the_unmasked_pairs():
+    """Brute-force count of the (row, key) pairs the masks leave valid."""
+    rng = np.random.default_rng(0)
+    for causal in (False, True):
+        for Nq, Nk in ((7, 7), (5, 9), (9, 5)):
+            lens = rng.integers(0, Nk + 1, size=3)
+            n = 0
+            for L in lens:
+                for i in range(Nq):
+                    for j in range(Nk):
+                        n += j < L and (not causal or j <= i + Nk - Nq)
+            H, d = 2, 8
+            assert bench.effective_flops(3, H, Nq, Nk, d, causal, lens) == 4.0 * H * d * n
+    # no padding, causal, square: half the nominal count plus the diagonal
+    assert bench.effective_flops(1, 1, 8, 8, 1, True) == 4.0 * 36
+
+
+def test_launch_stats():
+    st = bench.launch_stats(np.arange(1.0, 101.0))
+    assert st["median_ms"] == 50.5 and st["launches"] == 100
+    assert abs(st["p10_ms"] - 10.9) < 1e-9 and abs(st["p90_ms"] - 90.1) < 1e-9
