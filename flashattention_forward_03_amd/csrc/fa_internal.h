@@ -91,10 +91,10 @@ hipError_t launch_ln_fold(const float *gamma, const float *beta, const void *w, 
 long long gemm_grid_size(int M, int N);
 hipError_t launch_gemm(const GemmArgs &g, int epi, bool bf16, hipStream_t stream);
 
-// Decode: cached tokens per split-KV chunk, and the launch.
+// Decode: pages per split-KV chunk that the workspace is sized for (the
+// kernels use chunks of 8, 16 or 32 pages, never more partials than 8-page
+// chunks give), and the launch.
 constexpr int kDecodeChunkPages = 8;
-// Query heads per K/V head from which decode always uses the matrix-core kernel.
-constexpr int kDecodeMfmaGroup = 8;
 inline int decode_max_chunks(int max_pages) { return (max_pages + kDecodeChunkPages - 1) / kDecodeChunkPages; }
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -187,7 +187,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const vo
  *               Token t of sequence s lives in page page_table[s][t / page_size],
  *               row t % page_size.
  *   page_table  device int32 [S, max_pages_per_seq]; entries beyond a sequence's
- *               pages are ignored (never read).  4-byte aligned
+ *               pages are ignored (their values are never used).  4-byte aligned
  *   kv_lens     device int32 [S]: number of cached tokens of each sequence, all of
  *               which the query attends to.  Clamped to [0, max_pages_per_seq *
  *               page_size].  A used table entry outside [0, num_pages) is clamped
