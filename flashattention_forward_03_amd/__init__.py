@@ -28,7 +28,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
+# FA_MI355X_LIB names another build of the library to load instead (the
+# host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("FA_MI355X_LIB") or os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_OK = 0
 FA_ERR_NULL = 1

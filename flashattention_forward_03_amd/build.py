@@ -48,14 +48,18 @@ def is_stale() -> bool:
     return any(os.path.getmtime(p) > t for p in _deps())
 
 
-def build(force: bool = True, verbose: bool = False, extra_flags=()) -> str:
-    if not force and not is_stale():
+def build(force: bool = True, verbose: bool = False, extra_flags=(), lib: str = LIB, build_dir: str = BUILD_DIR,
+          link_flags=()) -> str:
+    """Compile every source and link ``lib``; ``extra_flags`` are added to each
+    compile line and ``link_flags`` to the link line (the host-sanitizer build
+    passes both and its own output paths)."""
+    if not force and lib == LIB and not is_stale():
         return LIB
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, *flags_for(src), *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd))
@@ -73,11 +77,11 @@ def build(force: bool = True, verbose: bool = False, extra_flags=()) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError("hipcc failed for " + ", ".join(failed))
-    tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+    tmp = lib + ".tmp"
+    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *link_flags, "-o", tmp],
                    check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -25,7 +25,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        # ORACLE_LIB names another build to load instead (the sanitizer build)
+        path = os.environ.get("ORACLE_LIB") or _build.build(force=False)
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
