@@ -2,9 +2,9 @@
 against the fp64 oracle, through the C ABI binding.  Query head h reads K/V
 head h // (H // H_kv): multi-query (H_kv = 1) and grouped-query attention as
 compared in the llm-kernel-lib page's "Ablation Study".  Decode takes the
-matrix-core kernel from 8 query heads per K/V head (and from 4 when there are
-at most 64 (sequence, K/V head) pairs), the dot-product kernel otherwise: the
-cases below cover both."""
+16x16 page-step kernel up to 16 query heads per K/V head and the 32x32 kernel
+for wider groups (32-head slices): the cases below cover both, with padded
+slices (group sizes that are not a power of two)."""
 import math
 
 import numpy as np
