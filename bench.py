@@ -26,7 +26,7 @@ decode batch; beside each, the fp64 oracle's wall time on the host cores
 (one thread too for the B1 H1 configs and the decode) and the parity of the
 GPU output over every element.  ``cpu_baseline`` is the oracle on the
 headline workload (every row, all host cores up to 16).
-``backward`` times fa_bwd (D pass, dK/dV pass, dQ pass) on the headline
+``backward`` times fa_bwd (the dQ pass with the row term D, then the dK/dV pass) on the headline
 shape outside the step: nominal FLOPs 2.5x the forward's (five products of
 the forward's size against two).
 ``kv_append`` times fa_kv_append writing the whole grouped-query decode batch

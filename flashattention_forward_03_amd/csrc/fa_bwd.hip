@@ -2,10 +2,11 @@
 //
 // Method (gpu-inference page, section 02): the probabilities are recomputed
 // from the forward's saved log-sum-exp instead of being stored, and the work
-// splits into three kernels: a row term D_i = dO_i . O_i, a pass that owns a
-// block of keys and accumulates dK and dV over the query rows that see them,
-// and a pass that owns a block of query rows and accumulates dQ over their
-// keys.  With P_ij = exp(scale q_i.k_j - LSE_i) (zero where masked):
+// splits into a row term D_i = dO_i . O_i, a pass that owns a block of query
+// rows and accumulates dQ over their keys, and a pass that owns a block of
+// keys and accumulates dK and dV over the query rows that see them.  The row
+// term is formed by the dQ pass, which holds each row's dO anyway, and
+// written out for the dK/dV pass, which runs after it.  With P_ij = exp(scale q_i.k_j - LSE_i) (zero where masked):
 //   dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i),
 //   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
 // Every gradient is written once by the block that owns it (no atomics), so
@@ -16,7 +17,8 @@
 // register chaining as the forward (an accumulator's registers are the next
 // MFMA's B operand once the rows of the first product are permuted by sigma):
 //   * dQ pass: a workgroup = 4 waves x 32 query rows; Q and dO rows are held
-//     as B operands; K and V tiles of 32 keys stream through a three-slot LDS
+//     as B operands, and D_i = dO_i . O_i is formed from the dO operands and
+//     the O row before the loop; K and V tiles of 32 keys stream through a three-slot LDS
 //     ring (buffer-to-LDS copies).  Per tile: S^T = K Q^T, dP^T = V dO^T,
 //     P^T and dS^T lane-local (each lane owns a query row, so LSE_i and D_i
 //     are per-lane scalars), then dQ^T += K^T dS^T with K^T read by the
@@ -40,38 +42,13 @@ constexpr int BK = 128;        // keys per dK/dV workgroup (32 per wave)
 constexpr int BT = 32;         // rows per streamed tile
 constexpr int STAGES = 3;      // LDS ring depth (tiles)
 
-// ---------------------------------------------------------------- D pass ---
-
-// delta[r] = sum_t dO[r, t] * O[r, t]; d/8 lanes per row, 8 head dims each.
-template <int D, bool BF16>
-__global__ __launch_bounds__(NTHREADS) void bwd_delta_kernel(const float *__restrict__ O,
-                                                             const uint16_t *__restrict__ dO,
-                                                             float *__restrict__ delta, long long rows)
-{
-    constexpr int TPR = D / 8;
-    const long long row = (long long)blockIdx.x * (NTHREADS / TPR) + threadIdx.x / TPR;
-    const int gd = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const f32x4_t o0 = *reinterpret_cast<const f32x4_t *>(O + row * D + 8 * gd);
-        const f32x4_t o1 = *reinterpret_cast<const f32x4_t *>(O + row * D + 8 * gd + 4);
-        const u32x4_t g = load16(dO + row * D + 8 * gd);
-        acc = o0[0] * lo16<BF16>(g[0]) + o0[1] * hi16<BF16>(g[0]) + o0[2] * lo16<BF16>(g[1]) +
-              o0[3] * hi16<BF16>(g[1]) + o1[0] * lo16<BF16>(g[2]) + o1[1] * hi16<BF16>(g[2]) +
-              o1[2] * lo16<BF16>(g[3]) + o1[3] * hi16<BF16>(g[3]);
-    }
-    acc = TPR == 16 ? row16_sum(acc) : row8_sum(acc);
-    if (row < rows && gd == 0)
-        delta[row] = acc;
-}
-
 // ---------------------------------------------------------------- dQ pass ---
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
-    float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int n_qtiles, float c_log2, float scale,
+    const uint16_t *__restrict__ dO, const float *__restrict__ O, const float *__restrict__ LSE,
+    float *__restrict__ delta, float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int n_qtiles, float c_log2, float scale,
     int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
@@ -150,7 +127,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         if (i < n_tiles)
             issue(i);
 
-    // Q and dO rows of this lane's query (B operands), its LSE and D
+    // Q and dO rows of this lane's query (B operands), its LSE, and
+    // D = dO . O over the head dims this lane holds (8 per k-step), summed
+    // with the other half of the row held by lane ^ 32
     u32x4_t qf[G::KSTEPS], gf[G::KSTEPS];
     float lse2 = INFINITY, Di = 0.f;   // lse2 = +inf makes P = 0 (rows past Nq, rows without keys)
     {
@@ -158,17 +137,30 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         const size_t r = qbase + (ok ? qrow : 0);
         const uint16_t *qp = Q + r * D + 8 * hh;
         const uint16_t *gp = dO + r * D + 8 * hh;
+        const float *op = O + r * D + 8 * hh;
+        f32x4_t of[G::KSTEPS][2];
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
             qf[c] = ok ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
             gf[c] = ok ? load16(gp + 16 * c) : u32x4_t{0, 0, 0, 0};
+            of[c][0] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c) : f32x4_t{};
+            of[c][1] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c + 4) : f32x4_t{};
         }
         if (ok) {
             const float l = LSE[r];
             if (l > -INFINITY)
                 lse2 = l * kLog2e;
-            Di = delta[r];
         }
+        float dpart = 0.f;
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dpart = fmaf(of[c][j >> 1][2 * (j & 1)], lo16<BF16>(gf[c][j]),
+                             fmaf(of[c][j >> 1][2 * (j & 1) + 1], hi16<BF16>(gf[c][j]), dpart));
+        Di = dpart + other_half(dpart);
+        if (ok && hh == 0)
+            delta[r] = Di;
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
             asm volatile("" : "+v"(qf[c]));
@@ -508,14 +500,16 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 template <int D, bool BF16>
 hipError_t launch(const BwdArgs &a, hipStream_t stream)
 {
-    const long long rows = (long long)a.B * a.H * a.Nq;
-    const int rows_per_wg = NTHREADS / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
-                       dim3(NTHREADS), 0, stream, a.o, (const uint16_t *)a.dout, a.delta, rows);
+    const float c_log2 = a.scale * kLog2e;
+    // dQ first: it also writes the row term D that the dK/dV pass reads
+    const int n_qtiles = (a.Nq + BQ - 1) / BQ;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
+                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.dq, a.H, a.Hkv, a.Nq, a.Nk, n_qtiles,
+                       c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const float c_log2 = a.scale * kLog2e;
     const int n_ktiles = (a.Nk + BK - 1) / BK;
     if (n_ktiles > 0) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
@@ -523,15 +517,8 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
                            (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse, a.delta, a.dk, a.dv, a.H,
                            a.Hkv, a.Nq, a.Nk, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
         e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
     }
-    const int n_qtiles = (a.Nq + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
-                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, a.lse, a.delta, a.dq, a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, c_log2,
-                       a.scale, a.causal ? 1 : 0, a.kv_lens);
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace
@@ -540,8 +527,7 @@ long long bwd_grid_size(int B, int H, int Nq, int Nk)
 {
     const long long a = (long long)((Nq + BQ - 1) / BQ) * B * H;
     const long long c = (long long)((Nk + BK - 1) / BK) * B * H;
-    const long long r = ((long long)B * H * Nq + 7) / 8;
-    return a > c ? (a > r ? a : r) : (c > r ? c : r);
+    return a > c ? a : c;
 }
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)

@@ -46,8 +46,8 @@ struct DecodeArgs {
 long long fwd_grid_size(int B, int H, int Nq);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
-// Backward (contiguous [B, heads, N, d] tensors, d = 64 or 128): D = rowsum(dO * O)
-// into delta, then dK/dV and dQ.
+// Backward (contiguous [B, heads, N, d] tensors, d = 64 or 128): dQ, with
+// D = rowsum(dO * O) into delta, then dK/dV.
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *o, *lse;

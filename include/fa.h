@@ -150,8 +150,9 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
 
 /*
  * Exact attention backward from the forward's saved log-sum-exp (gpu-inference
- * page, section 02: the probabilities are recomputed, not stored; three
- * passes: the row term D, then dK/dV, then dQ).  With P the forward's masked
+ * page, section 02: the probabilities are recomputed, not stored; the row
+ * term D, dK/dV and dQ.  Here the dQ pass also forms D, then the dK/dV pass
+ * runs).  With P the forward's masked
  * softmax probabilities and dout = dL/dO:
  *   delta[i] = D_i = dO_i . O_i
  *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . v_j - D_i),
@@ -164,8 +165,8 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
  *   dq       [B, H, Nq, d] float32 output; 16-byte aligned
  *   dk, dv   [B, H_kv, Nk, d] float32 outputs (summed over the query heads that
  *            share each K/V head); 16-byte aligned
- *   delta    [B, H, Nq] float32, written with D (caller-owned scratch that the
- *            dK/dV and dQ passes read); 4-byte aligned
+ *   delta    [B, H, Nq] float32, written with D (caller-owned scratch: the dQ
+ *            pass writes it, the dK/dV pass reads it); 4-byte aligned
  *   d        64 or 128 (other head dims: FA_ERR_UNSUPPORTED)
  *   scale, causal, kv_lens: as for the forward that produced o and lse.
  *
