@@ -395,7 +395,8 @@ def time_backward(fa, dev, q, k, v, o, lse, w, steps, warmup):
     Nk = k.shape[2]
     fa.forward(q, k, v, scale=w.scale, causal=w.causal, out=(o, lse))
     outs = (torch.empty_like(o), torch.empty(k.shape, dtype=torch.float32, device=dev),
-            torch.empty(v.shape, dtype=torch.float32, device=dev), torch.empty_like(lse))
+            torch.empty(v.shape, dtype=torch.float32, device=dev),
+            torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device=dev))
     st = launch_stats(event_times(
         lambda: fa.backward(q, k, v, o, lse, dout, scale=w.scale, causal=w.causal, out=outs),
         warmup, steps))

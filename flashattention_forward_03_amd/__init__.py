@@ -397,7 +397,9 @@ def backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bo
     """Gradients of the forward: q, dout [B, H, Nq, d]; k, v [B, H_kv, Nk, d]
     (f16/bf16, contiguous); o [B, H, Nq, d] and lse [B, H, Nq] float32 from
     the forward on the same inputs.  Returns (dq, dk, dv) float32 (dk, dv
-    summed over the query heads sharing a K/V head) and the row term delta.
+    summed over the query heads sharing a K/V head) and the row term delta
+    [B, H, Nq] (D = dO . O, a view of the [2, B, H, Nq] scratch the library
+    fills; ``out`` supplies dq, dk, dv and that scratch).
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
@@ -427,16 +429,18 @@ def backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bo
         dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
         dk = torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device)
         dv = torch.empty_like(dk)
-        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        delta = torch.empty((2, B, H, Nq), dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv, delta = out
+        if tuple(delta.shape) != (2, B, H, Nq) or delta.dtype != torch.float32 or not delta.is_contiguous():
+            raise ValueError("out[3] (the row-term scratch) must be contiguous float32 [2, B, H, Nq]")
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B,
                 H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), kl_ptr, dt,
                 _stream_handle(stream))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
-    return dq, dk, dv, delta
+    return dq, dk, dv, delta[0]
 
 
 class Pager:

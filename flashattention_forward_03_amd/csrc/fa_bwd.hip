@@ -6,7 +6,8 @@
 // rows and accumulates dQ over their keys, and a pass that owns a block of
 // keys and accumulates dK and dV over the query rows that see them.  The row
 // term is formed by the dQ pass, which holds each row's dO anyway, and
-// written out for the dK/dV pass, which runs after it.  With P_ij = exp(scale q_i.k_j - LSE_i) (zero where masked):
+// written out for the dK/dV pass, which runs after it, together with the
+// row's LSE in base-2 units (so that pass forms P with one FMA per element).  With P_ij = exp(scale q_i.k_j - LSE_i) (zero where masked):
 //   dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i),
 //   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
 // Every gradient is written once by the block that owns it (no atomics), so
@@ -24,10 +25,12 @@
 //     are per-lane scalars), then dQ^T += K^T dS^T with K^T read by the
 //     transposing LDS read.
 //   * dK/dV pass: a workgroup = 4 waves x 32 keys; K and V rows are held as B
-//     operands; Q and dO tiles of 32 rows, and their LSE and D values, stream
-//     through the ring.  Per tile: S = Q K^T and dP = dO V^T with a lane
-//     owning a key column, P and dS with the rows' LSE / D read from LDS,
-//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+//     operands, V negated; Q and dO tiles of 32 rows, and their LSE and D
+//     values, stream through the ring.  Per tile: S = Q K^T and
+//     D - dP = D + dO (-V)^T (the dP product starts from D, so dS needs one
+//     multiply) with a lane owning a key column, P with the rows' LSE read
+//     from LDS, then dV^T += dO^T P and (-dK)^T += Q^T (-dS) with dO^T, Q^T
+//     read transposed; dK is stored with -scale.
 #include <climits>
 
 #include "fa_common.h"
@@ -146,8 +149,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
             of[c][0] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c) : f32x4_t{};
             of[c][1] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c + 4) : f32x4_t{};
         }
+        float l = -INFINITY;
         if (ok) {
-            const float l = LSE[r];
+            l = LSE[r];
             if (l > -INFINITY)
                 lse2 = l * kLog2e;
         }
@@ -159,8 +163,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
                 dpart = fmaf(of[c][j >> 1][2 * (j & 1)], lo16<BF16>(gf[c][j]),
                              fmaf(of[c][j >> 1][2 * (j & 1) + 1], hi16<BF16>(gf[c][j]), dpart));
         Di = dpart + other_half(dpart);
-        if (ok && hh == 0)
+        if (ok && hh == 0) {
+            // delta[0] = D, delta[1] = LSE * log2(e) (-inf stays -inf) for the dK/dV pass
             delta[r] = Di;
+            delta[(size_t)(gridDim.x / n_qtiles) * Nq + r] = l * kLog2e;
+        }
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
             asm volatile("" : "+v"(qf[c]));
@@ -274,10 +281,10 @@ __device__ __forceinline__ void dma_dword_lds(const u32x4s_t &rsrc, unsigned vof
 }
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
-    float *__restrict__ dK, float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int n_ktiles, float c_log2,
+    const uint16_t *__restrict__ dO, const float *__restrict__ delta, float *__restrict__ dK,
+    float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int n_ktiles, float c_log2,
     float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
@@ -301,6 +308,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int kt = blockIdx.x / BHn;
     const int b = g / Hkv, kvh = g - b * Hkv;
     const int grp = H / Hkv;
+    const size_t n_rows = (size_t)(BHn / Hkv) * H * Nq;   // B * H * Nq: delta[1] starts here
     int kvlen = Nk;
     if (kv_lens) {
         kvlen = kv_lens[b];
@@ -320,7 +328,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         n_qt = 0;
     const int n_tiles = n_qt > 0 ? n_qt * grp : 0;   // (query head, query tile) pairs
 
-    // K and V rows of this lane's key (B operands)
+    // K and -V rows of this lane's key (B operands; the sign flip of a
+    // 16-bit value is exact)
     u32x4_t kf[G::KSTEPS], vf[G::KSTEPS];
     {
         const bool ok = key < kvlen;   // padded keys: zero operands (their P and dS are masked)
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
             kf[c] = ok ? load16(K + r + 16 * c) : u32x4_t{0, 0, 0, 0};
-            vf[c] = ok ? load16(V + r + 16 * c) : u32x4_t{0, 0, 0, 0};
+            vf[c] = ok ? load16(V + r + 16 * c) ^ 0x80008000u : u32x4_t{0, 0, 0, 0};
         }
     }
 
@@ -355,8 +364,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const int rows = Nq - qt_begin * BT;
         qr = make_rsrc(Q + row0 * D, rows * G::ROWB);
         gr = make_rsrc(dO + row0 * D, rows * G::ROWB);
-        lr = make_rsrc(LSE + row0, rows * 4);
-        dr = make_rsrc(delta + row0, rows * 4);
+        lr = make_rsrc(delta + n_rows + row0, rows * 4);   // LSE * log2(e)
+        dr = make_rsrc(delta + row0, rows * 4);            // D
     };
     auto advance = [](u32x4s_t &r, uint32_t bytes) {
         const uint64_t base = (((uint64_t)r[1]) << 32 | r[0]) + bytes;
@@ -418,27 +427,32 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         // wave-uniform: does any query of this tile see any key of this wave?
         const bool live = kw0 < lim_key && (!causal || kw0 <= q0 + BT - 1 + dq);
         if (live) {
-            f32x16_t s[1], dp[1];
-            qk_tile<D, BF16>(qring[cur], qrow_perm, hh, kf, s);    // S = Q K^T
-            qk_tile<D, BF16>(gring[cur], qrow_perm, hh, vf, dp);   // dP = dO V^T
-            __builtin_amdgcn_sched_barrier(0);
             // this lane's rows: register r is query q0 + 16*(r/8) + 8*hh + r%8
             const float *ls = reinterpret_cast<const float *>(sring[cur][wave][0]);
             const float *ds = reinterpret_cast<const float *>(sring[cur][wave][1]);
+            f32x16_t s[1], dp[1];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4_t da = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh);
+                const f32x4_t dbv = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    dp[0][8 * h2 + e] = e < 4 ? da[e] : dbv[e - 4];
+            }
+            qk_tile<D, BF16>(qring[cur], qrow_perm, hh, kf, s);            // S = Q K^T
+            qk_tile_acc<D, BF16>(gring[cur], qrow_perm, hh, vf, dp);       // D - dP = D + dO (-V)^T
+            __builtin_amdgcn_sched_barrier(0);
+            // P, and -dS = P (D - dP)
             float p[16], dsv[16];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const f32x4_t la = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh);
                 const f32x4_t lb = *reinterpret_cast<const f32x4_t *>(ls + 16 * h2 + 8 * hh + 4);
-                const f32x4_t da = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh);
-                const f32x4_t dbv = *reinterpret_cast<const f32x4_t *>(ds + 16 * h2 + 8 * hh + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int r = 8 * h2 + e;
-                    const float lse = e < 4 ? la[e] : lb[e - 4];
-                    const float dd = e < 4 ? da[e] : dbv[e - 4];
-                    p[r] = fast_exp2(fmaf(s[0][r], c_log2, -lse * kLog2e));
-                    dsv[r] = p[r] * (dp[0][r] - dd);
+                    p[r] = fast_exp2(fmaf(s[0][r], c_log2, -(e < 4 ? la[e] : lb[e - 4])));
+                    dsv[r] = p[r] * dp[0][r];
                 }
             }
             // wave-uniform: may any element of this block be masked?  (p and
@@ -467,7 +481,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             pv_mfma<D, BF16>(ta, pf, dvacc);                  // dV^T += dO^T P
             __builtin_amdgcn_sched_barrier(0);
             pv_operands<D, true>(qring[cur], lane, hh, ta);   // Q^T
-            pv_mfma<D, BF16>(ta, dsf, dkacc);                 // dK^T += Q^T dS
+            pv_mfma<D, BF16>(ta, dsf, dkacc);                 // (-dK)^T += Q^T (-dS)
         }
     };
     int t = 0;
@@ -484,13 +498,14 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
     if (key < Nk) {
         const size_t r = ((size_t)g * Nk + key) * D + 4 * hh;
+        const float kscale = -scale;   // the accumulator holds -dK / scale
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<f32x4_t *>(dK + r + 32 * db + 8 * q) =
-                    f32x4_t{dkacc[db][4 * q] * scale, dkacc[db][4 * q + 1] * scale, dkacc[db][4 * q + 2] * scale,
-                            dkacc[db][4 * q + 3] * scale};
+                    f32x4_t{dkacc[db][4 * q] * kscale, dkacc[db][4 * q + 1] * kscale,
+                            dkacc[db][4 * q + 2] * kscale, dkacc[db][4 * q + 3] * kscale};
                 *reinterpret_cast<f32x4_t *>(dV + r + 32 * db + 8 * q) =
                     f32x4_t{dvacc[db][4 * q], dvacc[db][4 * q + 1], dvacc[db][4 * q + 2], dvacc[db][4 * q + 3]};
             }
@@ -501,20 +516,24 @@ template <int D, bool BF16>
 hipError_t launch(const BwdArgs &a, hipStream_t stream)
 {
     const float c_log2 = a.scale * kLog2e;
-    // dQ first: it also writes the row term D that the dK/dV pass reads
+    // dQ first: it also writes the row term D and LSE * log2(e), which the
+    // dK/dV pass reads
     const int n_qtiles = (a.Nq + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)), dim3(NTHREADS),
-                       0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.dq, a.H, a.Hkv, a.Nq, a.Nk, n_qtiles,
-                       c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    hipError_t e = hipSuccess;
+    if (n_qtiles > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)),
+                           dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                           (const uint16_t *)a.v, (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.dq, a.H,
+                           a.Hkv, a.Nq, a.Nk, n_qtiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     const int n_ktiles = (a.Nk + BK - 1) / BK;
     if (n_ktiles > 0) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
                            dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
-                           (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse, a.delta, a.dk, a.dv, a.H,
+                           (const uint16_t *)a.v, (const uint16_t *)a.dout, a.delta, a.dk, a.dv, a.H,
                            a.Hkv, a.Nq, a.Nk, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
         e = hipGetLastError();
     }

@@ -204,6 +204,30 @@ __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk
             s[blk] = c == 0 ? mma32<BF16>(ka[blk][c], qf[c], f32x16_t{}) : mma32<BF16>(ka[blk][c], qf[c], s[blk]);
 }
 
+// qk_tile accumulating onto the values already in s (the first product of
+// the tile starts from them instead of zero).
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile_acc(const unsigned char *kb, int krow_in_blk, int hh,
+                                            const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
+{
+    using G = Geometry<D>;
+    u32x4_t ka[G::NBLK][G::KSTEPS];
+#pragma unroll
+    for (int blk = 0; blk < G::NBLK; ++blk) {
+        const int row = blk * 32 + krow_in_blk;
+        const unsigned char *rp = kb + row * G::ROWB;
+        const int sw = swz_k(row);
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            ka[blk][c] = *reinterpret_cast<const u32x4_t *>(rp + (swz_slot<G::DC>(2 * c + hh, sw) << 4));
+    }
+#pragma unroll
+    for (int c = 0; c < G::KSTEPS; ++c)
+#pragma unroll
+        for (int blk = 0; blk < G::NBLK; ++blk)
+            s[blk] = mma32<BF16>(ka[blk][c], qf[c], s[blk]);
+}
+
 // V^T operands of the P V MFMAs of one tile (A operand: row = column of O,
 // k = 8 consecutive tile keys), read with the transposing LDS read.  KSWZ:
 // the tile was stored with the row-read swizzle swz_k (a tile that is also

@@ -165,8 +165,9 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
  *   dq       [B, H, Nq, d] float32 output; 16-byte aligned
  *   dk, dv   [B, H_kv, Nk, d] float32 outputs (summed over the query heads that
  *            share each K/V head); 16-byte aligned
- *   delta    [B, H, Nq] float32, written with D (caller-owned scratch: the dQ
- *            pass writes it, the dK/dV pass reads it); 4-byte aligned
+ *   delta    [2, B, H, Nq] float32 caller-owned scratch, 4-byte aligned: the dQ
+ *            pass writes delta[0] = D and delta[1] = LSE * log2(e) (-inf stays
+ *            -inf), the dK/dV pass reads both
  *   d        64 or 128 (other head dims: FA_ERR_UNSUPPORTED)
  *   scale, causal, kv_lens: as for the forward that produced o and lse.
  *

@@ -138,3 +138,24 @@ def test_backward_d128_end_to_end():
     """End-to-end at d = 128: the GPU forward's O and LSE into the backward."""
     w = gen.fwd_inputs(2, 4, 250, 250, 128, "bf16", seed=12950, causal=True, Hkv=2)
     _check(w, _dout(w, 12951), "bwd d128 end-to-end", fwd="gpu")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(0, 70), (70, 0)])
+def test_backward_empty_side(Nq, Nk):
+    """No query rows: dK = dV = 0 (no row sees the keys).  No keys: dQ = 0 and
+    D = 0 (the forward's O is 0 for rows without keys)."""
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    B, H, d = 2, 2, 64
+    q = torch.randn(B, H, Nq, d, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, device="cuda").to(torch.bfloat16)
+    g = torch.randn(B, H, Nq, d, device="cuda").to(torch.bfloat16)
+    o = torch.zeros(B, H, Nq, d, device="cuda")
+    lse = torch.full((B, H, Nq), float("-inf"), device="cuda")
+    dq, dk, dv, delta = fa.backward(q, k, v, o, lse, g, causal=False)
+    torch.cuda.synchronize()
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+        assert not torch.any(x != 0), f"{name} not zero"
