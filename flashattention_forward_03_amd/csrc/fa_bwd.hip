@@ -19,7 +19,8 @@
 // MFMA's B operand once the rows of the first product are permuted by sigma):
 //   * dQ pass: a workgroup = 4 waves x 32 query rows; Q and dO rows are held
 //     as B operands, and D_i = dO_i . O_i is formed from the dO operands and
-//     the O row before the loop; K and V tiles of 32 keys stream through a three-slot LDS
+//     the O row before the loop (-D_i, kept in 16 registers, is where each
+//     tile's dP product starts); K and V tiles of 32 keys stream through a three-slot LDS
 //     ring (buffer-to-LDS copies).  Per tile: S^T = K Q^T, dP^T = V dO^T,
 //     P^T and dS^T lane-local (each lane owns a query row, so LSE_i and D_i
 //     are per-lane scalars), then dQ^T += K^T dS^T with K^T read by the
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     // with the other half of the row held by lane ^ 32
     u32x4_t qf[G::KSTEPS], gf[G::KSTEPS];
     float lse2 = INFINITY, Di = 0.f;   // lse2 = +inf makes P = 0 (rows past Nq, rows without keys)
+    f32x16_t dneg;                     // -D in every register: the start of the dP product
     {
         const bool ok = qrow < Nq;
         const size_t r = qbase + (ok ? qrow : 0);
@@ -163,6 +165,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
                 dpart = fmaf(of[c][j >> 1][2 * (j & 1)], lo16<BF16>(gf[c][j]),
                              fmaf(of[c][j >> 1][2 * (j & 1) + 1], hi16<BF16>(gf[c][j]), dpart));
         Di = dpart + other_half(dpart);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dneg[r] = -Di;
         if (ok && hh == 0) {
             // delta[0] = D, delta[1] = LSE * log2(e) (-inf stays -inf) for the dK/dV pass
             delta[r] = Di;
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
             const int kt0 = t * BT;
             f32x16_t s[1], dp[1];
             qk_mma<D, BF16>(ka0, qf, s);    // S^T = K Q^T
-            qk_mma<D, BF16>(va0, gf, dp);   // dP^T = V dO^T
+            qk_mma_from<D, BF16>(va0, gf, dp, dneg);   // (dP - D)^T = V dO^T - D
             __builtin_amdgcn_sched_barrier(0);
             if (!fast && t >= mask_t)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
                     const int r = 8 * h2 + 2 * q;
                     const float p0 = fast_exp2(fmaf(s[0][r], c_log2, -lse2));
                     const float p1 = fast_exp2(fmaf(s[0][r + 1], c_log2, -lse2));
-                    dsf[h2][q] = pack2<BF16>(p0 * (dp[0][r] - Di), p1 * (dp[0][r + 1] - Di));
+                    dsf[h2][q] = pack2<BF16>(p0 * dp[0][r], p1 * dp[0][r + 1]);
                 }
             __builtin_amdgcn_sched_barrier(0);
             u32x4_t ka[G::DB][G::PCH];

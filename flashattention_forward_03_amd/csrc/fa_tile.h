@@ -182,6 +182,19 @@ __device__ __forceinline__ void qk_mma(const u32x4_t (&ka)[kBN<D> / 32][D / 16],
             s[blk] = c == 0 ? mma32<BF16>(ka[blk][c], qf[c], f32x16_t{}) : mma32<BF16>(ka[blk][c], qf[c], s[blk]);
 }
 
+// qk_mma starting from the accumulator values `from` (read, not changed).
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_mma_from(const u32x4_t (&ka)[kBN<D> / 32][D / 16], const u32x4_t (&qf)[D / 16],
+                                            f32x16_t (&s)[kBN<D> / 32], const f32x16_t &from)
+{
+    using G = Geometry<D>;
+#pragma unroll
+    for (int c = 0; c < G::KSTEPS; ++c)
+#pragma unroll
+        for (int blk = 0; blk < G::NBLK; ++blk)
+            s[blk] = mma32<BF16>(ka[blk][c], qf[c], c == 0 ? from : s[blk]);
+}
+
 template <int D, bool BF16>
 __device__ __forceinline__ void qk_tile(const unsigned char *kb, int krow_in_blk, int hh,
                                         const u32x4_t (&qf)[D / 16], f32x16_t (&s)[kBN<D> / 32])
