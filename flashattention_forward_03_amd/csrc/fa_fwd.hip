@@ -38,6 +38,8 @@
 //     LSE = m + ln l, and the max and the O rescale are skipped on almost
 //     every tile;
 //   * O is written in fp32 [B, H, Nq, d], LSE = m * scale + ln(l) in fp32.
+#include <cstdlib>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 #include "fa_tile.h"
@@ -332,6 +334,200 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd
                           kbuf, vbuf, wave, lane);
 }
 
+// Small grids (few heads, short or single sequences): the tiled kernel above
+// gives each (b, h, 128-row query tile) to one workgroup, which leaves most
+// of the 256 CUs idle and makes every wave walk all keys of its rows in one
+// chain.  Here a workgroup owns one 32-row query block and its four waves
+// split the block's key tiles between them (tile t goes to wave t % 4), each
+// with its own two-slot LDS ring and no barrier in the loop; at the end the
+// four partial (O, m, l) are merged through LDS with the log-sum-exp rule, as
+// the split-KV decode merges its chunks (NanoInfer page "Online Softmax": the
+// same recurrence over blocks).
+constexpr int SPLIT_ROWS = 32;
+constexpr int SPLIT_ST = 2;   // ring slots per wave
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    void *__restrict__ O, float *__restrict__ LSE, FwdLayout lay, int H, int Hkv, int Nq, int Nk, int n_qblocks,
+    float c_log2, int causal_flag, const int32_t *__restrict__ kv_lens)
+{
+    using G = Geometry<D>;
+    constexpr int PPW = G::PIECES_PER_WAVE;
+    static_assert(4 * SPLIT_ST * 2 * G::TILE <= 160 * 1024, "LDS");
+    static_assert(4 * SPLIT_ROWS * D * 4 <= 4 * SPLIT_ST * 2 * G::TILE, "merge staging fits the rings");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[4][SPLIT_ST][2][G::TILE];   // [wave][slot][K, V]
+    __shared__ float mls[2][4][SPLIT_ROWS];                                                   // m * c, l per wave
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const bool causal = causal_flag != 0;
+
+    const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int bhi = logical / n_qblocks;
+    const int qb = logical - bhi * n_qblocks;
+    const int b = bhi / H;
+    const int h = bhi - b * H;
+    const int kvh = h / (H / Hkv);
+    int kvlen = Nk;
+    if (kv_lens) {
+        kvlen = kv_lens[b];
+        kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
+    }
+    const uint16_t *Qb = Q + b * lay.qs[0] + h * lay.qs[1];
+    const uint16_t *Kb = K + b * lay.ks[0] + kvh * lay.ks[1];
+    const uint16_t *Vb = V + b * lay.vs[0] + kvh * lay.vs[1];
+    const long long oe = b * lay.os[0] + h * lay.os[1];
+    const int d = lay.d;
+    const unsigned krs = (unsigned)(lay.ks[2] * 2), vrs = (unsigned)(lay.vs[2] * 2);
+
+    const int q0 = qb * SPLIT_ROWS;
+    const int dq = Nk - Nq;
+    const int qrow = q0 + l32;
+    constexpr int BN = G::BN;
+    int key_end = kvlen;
+    if (causal)
+        key_end = min(key_end, max(min(q0 + SPLIT_ROWS, Nq) - 1 + dq + 1, 0));
+    const int n_tiles = (key_end + BN - 1) / BN;
+    int mask_t = kvlen / BN;   // first tile that needs the mask
+    if (causal) {
+        const int x1 = q0 + dq + 1;
+        mask_t = min(mask_t, x1 <= 0 ? 0 : x1 / BN);
+    }
+    int lim = kvlen;
+    if (causal)
+        lim = min(lim, qrow + dq + 1);
+    // this wave's tiles: t = wave, wave + 4, ...
+    const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
+
+    f32x16_t oacc[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+        oacc[db] = f32x16_t{};
+    RowState st{-INFINITY, 0.f, -INFINITY};
+    const float tau_log2 = kRescaleLog2<BF16>;
+    int ko[G::NBLK][G::KSTEPS];
+    qk_offsets<D>(sigma(l32), hh, ko);
+    const u32x4s_t krsrc = make_rsrc(Kb, kvlen * krs), vrsrc = make_rsrc(Vb, kvlen * vrs);
+    // the whole tile is copied by this wave: the pieces of the four copy
+    // lanes sets of the tiled kernel (piece u of set w lands at w * 1 KB + u * 4 KB)
+    unsigned koff[4][PPW], voff[4][PPW];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        dma_offsets<D, true>(w, lane, d, krs, koff[w]);
+        dma_offsets<D, false>(w, lane, d, vrs, voff[w]);
+    }
+    uint32_t klds[SPLIT_ST], vlds[SPLIT_ST];
+#pragma unroll
+    for (int i = 0; i < SPLIT_ST; ++i) {
+        klds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)&ring[wave][i][0][0]);
+        vlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)&ring[wave][i][1][0]);
+    }
+    auto issue = [&](int t, int slot) {   // key tile t into this wave's slot
+        const uint64_t kb = (((uint64_t)krsrc[1] << 32) | krsrc[0]) + (uint64_t)t * BN * krs;
+        const uint64_t vb = (((uint64_t)vrsrc[1] << 32) | vrsrc[0]) + (uint64_t)t * BN * vrs;
+        const u32x4s_t kr = {(uint32_t)kb, (uint32_t)(kb >> 32), krsrc[2] - (uint32_t)(t * BN) * krs, krsrc[3]};
+        const u32x4s_t vr = {(uint32_t)vb, (uint32_t)(vb >> 32), vrsrc[2] - (uint32_t)(t * BN) * vrs, vrsrc[3]};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            dma_tile_lds<D>(kr, koff[w], klds[slot] + w * 1024);
+            dma_tile_lds<D>(vr, voff[w], vlds[slot] + w * 1024);
+        }
+    };
+    if (my_tiles > 0)
+        issue(wave, 0);
+
+    u32x4_t qf[G::KSTEPS];
+    {
+        const uint16_t *qp = Qb + (qrow < Nq ? qrow : 0) * lay.qs[2] + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            qf[c] = (qrow < Nq && 16 * c + 8 * hh < d) ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < G::KSTEPS; ++c)
+            asm volatile("" : "+v"(qf[c]));
+    }
+
+    for (int j = 0; j < my_tiles; ++j) {
+        const int t = wave + 4 * j;
+        const int slot = j & 1;
+        // the other slot was read by this wave's previous tile (its MFMAs
+        // consumed the reads), so it can be refilled now
+        if (j + 1 < my_tiles) {
+            issue(t + 4, slot ^ 1);
+            wait_vmcnt<8 * PPW>();   // this tile's copies done, the next tile's in flight
+        } else {
+            wait_vmcnt<0>();
+        }
+        const unsigned char *kc = &ring[wave][slot][0][0];
+        const unsigned char *vc = &ring[wave][slot][1][0];
+        u32x4_t ka[G::NBLK][G::KSTEPS];
+        qk_read<D>(kc, ko, ka);
+        f32x16_t s[G::NBLK];
+        qk_mma<D, BF16>(ka, qf, s);
+        if (t >= mask_t)
+            mask_tile<D>(s, lim - (t * BN + 8 * hh));
+        u32x4_t pf[G::PCH];
+        float alpha;
+        if (__builtin_expect(softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha), 0))
+            rescale_acc<D>(oacc, alpha);
+        pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
+    }
+
+    // ---- merge of the four waves' partials: m*c and l per row, then O
+    const float l_tot = st.l + other_half(st.l);
+    __syncthreads();   // every wave is done with its ring: it becomes the staging area
+    if (hh == 0) {
+        mls[0][wave][l32] = st.mc;
+        mls[1][wave][l32] = l_tot;
+    }
+    float *stage = reinterpret_cast<float *>(&ring[0][0][0][0]);   // [wave][db][g][lane] f32x4
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4_t *>(stage + (((wave * G::DB + db) * 4 + g) * 64 + lane) * 4) =
+                f32x4_t{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+    __syncthreads();
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        mw[w] = mls[0][w][l32];
+        M = fmaxf(M, mw[w]);
+    }
+    float fw[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        fw[w] = M == -INFINITY ? 0.f : fast_exp2(mw[w] - M);   // a wave without keys of this row: mw = -inf, weight 0
+        L = fmaf(fw[w], mls[1][w][l32], L);
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (qrow < Nq) {
+        void *orow = lay.o_kind == FA_O_F32 ? (void *)(static_cast<float *>(O) + oe + qrow * lay.os[2])
+                                            : (void *)(static_cast<uint16_t *>(O) + oe + qrow * lay.os[2]);
+        // wave w merges and stores the (db, g) groups with (4 db + g) % 4 == w
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (g != wave)
+                    continue;
+                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    acc += fw[w] * *reinterpret_cast<const f32x4_t *>(stage + (((w * G::DB + db) * 4 + g) * 64 + lane) * 4);
+                const int dim0 = 32 * db + 8 * g + 4 * hh;
+                if (dim0 < d)
+                    store_o4(orow, dim0, lay.o_kind, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+            }
+        if (wave == 0 && hh == 0)
+            LSE[(size_t)bhi * Nq + qrow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
 int units_per_head(int Nq, bool causal)
 {
     const int n_qtiles = (Nq + BM - 1) / BM;
@@ -339,9 +535,39 @@ int units_per_head(int Nq, bool causal)
     return n_qtiles;
 }
 
+// Kernel choice: the split-key kernel when the tiled kernel would launch
+// fewer workgroups than the GPU has CUs (d = 96 excepted: its two-slot rings
+// per wave would not fit in LDS).  FA_FWD_SPLIT=0 / 1 in the environment
+// forces the tiled / split kernel (the tests run both on the same shapes).
+bool use_split(const FwdArgs &a, int D)
+{
+    if (D == 96)
+        return false;
+    const long long tiled = (long long)((a.Nq + BM - 1) / BM) * a.B * a.H;
+    if (tiled >= (1 << 20))   // keep the split grid (4x) far inside the 32-bit grid limit
+        return false;
+    const char *e = std::getenv("FA_FWD_SPLIT");
+    if (e && e[0] == '0' && e[1] == 0)
+        return false;
+    if (e && e[0] == '1' && e[1] == 0)
+        return true;
+    return tiled < 256;
+}
+
 template <int D, bool BF16>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
+    if constexpr (D != 96) {
+        if (use_split(a, D)) {
+            const int n_qblocks = (a.Nq + SPLIT_ROWS - 1) / SPLIT_ROWS;
+            const long long grid = (long long)n_qblocks * a.B * a.H;
+            hipLaunchKernelGGL((fwd_split_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
+                               (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
+                               a.lay, a.H, a.Hkv, a.Nq, a.Nk, n_qblocks, a.scale * kLog2e, a.causal ? 1 : 0,
+                               a.kv_lens);
+            return hipGetLastError();
+        }
+    }
     const int n_qtiles = (a.Nq + BM - 1) / BM;
     const int n_units = units_per_head(a.Nq, a.causal);
     const long long grid = (long long)n_units * a.B * a.H;
@@ -354,7 +580,9 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
 
 }  // namespace
 
-long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1) / BM) * B * H; }   // upper bound
+// upper bound of the tiled kernel's grid; the split-key kernel only runs when
+// that grid is below 256, so its own (4x) grid stays below 1024
+long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1) / BM) * B * H; }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {

@@ -99,6 +99,14 @@ extern "C" {
  * allowed (every row empty).  The keys of one (b, h) are addressed with
  * 32-bit byte offsets: (Nk + 64) * d * 2 must stay below 2^31, else
  * FA_ERR_SHAPE.  The library needs no workspace for this call.
+ *
+ * Two kernels compute this: a tiled one (a workgroup per 128-row query tile)
+ * and, when that would launch fewer than 256 workgroups (few heads, short or
+ * single sequences) and d > 96 or d <= 64, a split-key one (a workgroup per
+ * 32-row block whose four waves share out its keys and merge their partial
+ * results by the log-sum-exp rule).  Both give the same result up to rounding
+ * order.  The environment variable FA_FWD_SPLIT=0 or 1, read at each call,
+ * forces the tiled or the split-key kernel (for testing either on any shape).
  */
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
            int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype,

@@ -8,7 +8,7 @@ import fa_inputs as gen
 import oracle
 from parity import compare, device_tensors, gpu_forward, host_cores
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("fwd_kernel")]
 
 
 @pytest.fixture(scope="module", autouse=True)

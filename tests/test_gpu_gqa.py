@@ -15,7 +15,7 @@ import oracle
 from parity import compare, gpu_forward, host_cores
 from test_gpu_decode import ref_decode, run_decode
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("fwd_kernel")]
 
 
 # ----------------------------------------------------------------- forward

@@ -11,7 +11,7 @@ import fa_inputs as gen
 import oracle
 from parity import compare, gpu_forward, host_cores
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("fwd_kernel")]
 
 TORCH_DT = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}
 

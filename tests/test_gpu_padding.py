@@ -20,7 +20,7 @@ import fa_inputs as gen
 import oracle
 from parity import compare, compare_grad
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("fwd_kernel")]
 
 # IEEE bit patterns: quiet NaN, +Inf, -Inf
 POISON = {"bf16": (0x7FC0, 0x7F80, 0xFF80), "f16": (0x7E00, 0x7C00, 0xFC00)}

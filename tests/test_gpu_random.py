@@ -48,13 +48,13 @@ def _dev(bits, dtype, layout):
 
 
 @pytest.mark.parametrize("seed", range(40))
-def test_random_forward(seed):
+def test_random_forward(seed, fwd_kernel):
     import torch
 
     import flashattention_forward_03_amd as fa
 
     c = _fwd_case(31000 + seed)
-    print(f"forward case {seed}: {c}", flush=True)
+    print(f"forward case {seed} ({fwd_kernel} kernel): {c}", flush=True)
     w = gen.fwd_inputs(c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["dtype"], seed=32000 + seed,
                        causal=c["causal"], scale=1.0 / math.sqrt(c["d"]),
                        kv_len_range=(0, c["Nk"]) if c["padded"] else None, Hkv=c["Hkv"])
