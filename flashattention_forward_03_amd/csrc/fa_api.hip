@@ -185,7 +185,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const vo
         return FA_ERR_SHAPE;
     if (H > 0 && (H_kv < 1 || H % H_kv != 0))
         return FA_ERR_SHAPE;
-    if (d != 64 && d != 128)
+    if (d < 8 || d > 128 || d % 8 != 0)
         return FA_ERR_UNSUPPORTED;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_UNSUPPORTED;

@@ -14,7 +14,9 @@
 // results are bitwise reproducible.  dK and dV of a K/V head sum over the
 // query heads that share it (grouped-query attention).
 //
-// gfx950 mapping (d = 64 or 128), both passes on the 32x32x16 MFMA with the same
+// gfx950 mapping (a head dim d <= 64 runs on the d = 64 geometry, d <= 128 on the
+// 128 one: columns past d read as zero and are not stored; rows are d wide in
+// memory), both passes on the 32x32x16 MFMA with the same
 // register chaining as the forward (an accumulator's registers are the next
 // MFMA's B operand once the rows of the first product are permuted by sigma):
 //   * dQ pass: a workgroup = 4 waves x 32 query rows; Q and dO rows are held
@@ -52,12 +54,13 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ O, const float *__restrict__ LSE,
-    float *__restrict__ delta, float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int n_qtiles, float c_log2, float scale,
-    int causal_flag, const int32_t *__restrict__ kv_lens)
+    float *__restrict__ delta, float *__restrict__ dQ, int H, int Hkv, int Nq, int Nk, int d, int n_qtiles,
+    float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
     static_assert(G::BN == BT, "tile rows");
     constexpr int PER = 2 * G::PIECES_PER_WAVE;   // copies per lane per tile (K + V)
+    const unsigned rb = (unsigned)d * 2u;          // bytes per K/V row in memory
     __shared__ __attribute__((aligned(1024))) unsigned char kring[STAGES][G::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char vring[STAGES][G::TILE];
 
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         kvlen = kvlen < 0 ? 0 : (kvlen > Nk ? Nk : kvlen);
     }
     const size_t qbase = (size_t)bhi * Nq;
-    const uint16_t *Kb = K + ((size_t)b * Hkv + kvh) * Nk * D;
-    const uint16_t *Vb = V + ((size_t)b * Hkv + kvh) * Nk * D;
+    const uint16_t *Kb = K + ((size_t)b * Hkv + kvh) * Nk * d;
+    const uint16_t *Vb = V + ((size_t)b * Hkv + kvh) * Nk * d;
 
     const int q0 = qt * BQ;
     const int dq = Nk - Nq;
@@ -101,16 +104,16 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
 
     // ranges end at the last valid key: padded rows [kvlen, Nk) read as zero,
     // so their (masked) products add 0 * 0, never 0 * NaN from caller memory
-    const u32x4s_t krs = make_rsrc(Kb, kvlen * G::ROWB), vrs = make_rsrc(Vb, kvlen * G::ROWB);
+    const u32x4s_t krs = make_rsrc(Kb, kvlen * rb), vrs = make_rsrc(Vb, kvlen * rb);
     unsigned koff[G::PIECES_PER_WAVE], voff[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, koff);   // both tiles are read by rows
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, voff);
+    dma_offsets<D, true>(wave, lane, d, rb, koff);   // both tiles are read by rows
+    dma_offsets<D, true>(wave, lane, d, rb, voff);
     // copies of the next tile (in order) into ring slot st: resources at the
     // tile's first key, advanced by one tile per copy in scalar registers
     uint64_t kb_next = ((uint64_t)krs[1] << 32) | krs[0];
     uint64_t vb_next = ((uint64_t)vrs[1] << 32) | vrs[0];
     uint32_t range_next = krs[2];
-    constexpr uint32_t kTileBytes = (uint32_t)BT * G::ROWB;
+    const uint32_t kTileBytes = (uint32_t)BT * rb;
     uint32_t klds[STAGES], vlds[STAGES];
 #pragma unroll
     for (int i = 0; i < STAGES; ++i) {
@@ -140,16 +143,17 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     {
         const bool ok = qrow < Nq;
         const size_t r = qbase + (ok ? qrow : 0);
-        const uint16_t *qp = Q + r * D + 8 * hh;
-        const uint16_t *gp = dO + r * D + 8 * hh;
-        const float *op = O + r * D + 8 * hh;
+        const uint16_t *qp = Q + r * d + 8 * hh;
+        const uint16_t *gp = dO + r * d + 8 * hh;
+        const float *op = O + r * d + 8 * hh;
         f32x4_t of[G::KSTEPS][2];
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
-            qf[c] = ok ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
-            gf[c] = ok ? load16(gp + 16 * c) : u32x4_t{0, 0, 0, 0};
-            of[c][0] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c) : f32x4_t{};
-            of[c][1] = ok ? *reinterpret_cast<const f32x4_t *>(op + 16 * c + 4) : f32x4_t{};
+            const bool in = ok && 16 * c + 8 * hh < d;   // 8 columns, all inside d or all past it
+            qf[c] = in ? load16(qp + 16 * c) : u32x4_t{0, 0, 0, 0};
+            gf[c] = in ? load16(gp + 16 * c) : u32x4_t{0, 0, 0, 0};
+            of[c][0] = in ? *reinterpret_cast<const f32x4_t *>(op + 16 * c) : f32x4_t{};
+            of[c][1] = in ? *reinterpret_cast<const f32x4_t *>(op + 16 * c + 4) : f32x4_t{};
         }
         float l = -INFINITY;
         if (ok) {
@@ -260,14 +264,15 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     __syncthreads();
 
     if (qrow < Nq) {
-        float *op = dQ + (qbase + qrow) * D + 4 * hh;
+        float *op = dQ + (qbase + qrow) * d + 4 * hh;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<f32x4_t *>(op + 32 * db + 8 * g) =
-                    f32x4_t{acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
-                            acc[db][4 * g + 3] * scale};
+                if (32 * db + 8 * g < d)
+                    *reinterpret_cast<f32x4_t *>(op + 32 * db + 8 * g) =
+                        f32x4_t{acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                                acc[db][4 * g + 3] * scale};
     }
 }
 
@@ -289,10 +294,11 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ delta, float *__restrict__ dK,
-    float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int n_ktiles, float c_log2,
+    float *__restrict__ dV, int H, int Hkv, int Nq, int Nk, int d, int n_ktiles, float c_log2,
     float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
+    const unsigned rb = (unsigned)d * 2u;   // bytes per Q/dO row in memory
     static_assert(G::BN == BT, "tile rows");
     constexpr int PER = 2 * G::PIECES_PER_WAVE + 2;   // Q, dO pieces + LSE, D rows
     __shared__ __attribute__((aligned(1024))) unsigned char qring[STAGES][G::TILE];
@@ -338,11 +344,12 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     u32x4_t kf[G::KSTEPS], vf[G::KSTEPS];
     {
         const bool ok = key < kvlen;   // padded keys: zero operands (their P and dS are masked)
-        const size_t r = ((size_t)g * Nk + (ok ? key : 0)) * D + 8 * hh;
+        const size_t r = ((size_t)g * Nk + (ok ? key : 0)) * d + 8 * hh;
 #pragma unroll
         for (int c = 0; c < G::KSTEPS; ++c) {
-            kf[c] = ok ? load16(K + r + 16 * c) : u32x4_t{0, 0, 0, 0};
-            vf[c] = ok ? load16(V + r + 16 * c) ^ 0x80008000u : u32x4_t{0, 0, 0, 0};
+            const bool in = ok && 16 * c + 8 * hh < d;   // columns past d: zero operands
+            kf[c] = in ? load16(K + r + 16 * c) : u32x4_t{0, 0, 0, 0};
+            vf[c] = in ? load16(V + r + 16 * c) ^ 0x80008000u : u32x4_t{0, 0, 0, 0};
         }
     }
 
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     // copy in scalar registers (re-based when the head changes), so the lane
     // offsets are the tile-0 ones and no division runs per tile.
     unsigned qoff[G::PIECES_PER_WAVE];
-    dma_offsets<D, true>(wave, lane, D, G::ROWB, qoff);   // Q and dO tiles: same row layout
+    dma_offsets<D, true>(wave, lane, d, rb, qoff);   // Q and dO tiles: same row layout
     const unsigned roff = lane < 32 ? (unsigned)lane * 4u : kOutOfRange;
     uint32_t qlds[STAGES], glds[STAGES], llds[STAGES], dlds[STAGES];
 #pragma unroll
@@ -367,8 +374,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     auto set_head = [&](int j) {
         const size_t row0 = ((size_t)b * H + kvh * grp + j) * Nq + (size_t)qt_begin * BT;
         const int rows = Nq - qt_begin * BT;
-        qr = make_rsrc(Q + row0 * D, rows * G::ROWB);
-        gr = make_rsrc(dO + row0 * D, rows * G::ROWB);
+        qr = make_rsrc(Q + row0 * d, rows * rb);
+        gr = make_rsrc(dO + row0 * d, rows * rb);
         lr = make_rsrc(delta + n_rows + row0, rows * 4);   // LSE * log2(e)
         dr = make_rsrc(delta + row0, rows * 4);            // D
     };
@@ -390,8 +397,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
             if (++nx_j < grp)
                 set_head(nx_j);
         } else {
-            advance(qr, BT * G::ROWB);
-            advance(gr, BT * G::ROWB);
+            advance(qr, BT * rb);
+            advance(gr, BT * rb);
             advance(lr, BT * 4);
             advance(dr, BT * 4);
         }
@@ -502,12 +509,14 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     __syncthreads();
 
     if (key < Nk) {
-        const size_t r = ((size_t)g * Nk + key) * D + 4 * hh;
+        const size_t r = ((size_t)g * Nk + key) * d + 4 * hh;
         const float kscale = -scale;   // the accumulator holds -dK / scale
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (32 * db + 8 * q >= d)
+                    continue;
                 *reinterpret_cast<f32x4_t *>(dK + r + 32 * db + 8 * q) =
                     f32x4_t{dkacc[db][4 * q] * kscale, dkacc[db][4 * q + 1] * kscale,
                             dkacc[db][4 * q + 2] * kscale, dkacc[db][4 * q + 3] * kscale};
@@ -529,7 +538,7 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
         hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)((long long)n_qtiles * a.B * a.H)),
                            dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
                            (const uint16_t *)a.v, (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.dq, a.H,
-                           a.Hkv, a.Nq, a.Nk, n_qtiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
+                           a.Hkv, a.Nq, a.Nk, a.d, n_qtiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -539,7 +548,7 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)((long long)n_ktiles * a.B * a.Hkv)),
                            dim3(NTHREADS), 0, stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
                            (const uint16_t *)a.v, (const uint16_t *)a.dout, a.delta, a.dk, a.dv, a.H,
-                           a.Hkv, a.Nq, a.Nk, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
+                           a.Hkv, a.Nq, a.Nk, a.d, n_ktiles, c_log2, a.scale, a.causal ? 1 : 0, a.kv_lens);
         e = hipGetLastError();
     }
     return e;
@@ -556,7 +565,8 @@ long long bwd_grid_size(int B, int H, int Nq, int Nk)
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
 {
-    if (a.d == 128)
+    // LDS geometry of the smaller padded head dim (64 or 128) that holds d
+    if (a.d > 64)
         return a.bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
     return a.bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
 }

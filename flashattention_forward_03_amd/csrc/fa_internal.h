@@ -46,13 +46,13 @@ struct DecodeArgs {
 long long fwd_grid_size(int B, int H, int Nq);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 
-// Backward (contiguous [B, heads, N, d] tensors, d = 64 or 128): dQ, with
+// Backward (contiguous [B, heads, N, d] tensors, d = 8..128): dQ, with
 // D = rowsum(dO * O) into delta, then dK/dV.
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *o, *lse;
     float *dq, *dk, *dv, *delta;
-    int B, H, Hkv, Nq, Nk, d;   // d = 64 or 128
+    int B, H, Hkv, Nq, Nk, d;   // d = 8..128, a multiple of 8
     float scale;
     bool causal, bf16;
     const int32_t *kv_lens;

@@ -176,7 +176,8 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
  *   delta    [2, B, H, Nq] float32 caller-owned scratch, 4-byte aligned: the dQ
  *            pass writes delta[0] = D and delta[1] = LSE * log2(e) (-inf stays
  *            -inf), the dK/dV pass reads both
- *   d        64 or 128 (other head dims: FA_ERR_UNSUPPORTED)
+ *   d        8..128, a multiple of 8 (computed on the d = 64 or 128 tiles, the
+ *            columns past d as zeros); other head dims: FA_ERR_UNSUPPORTED
  *   scale, causal, kv_lens: as for the forward that produced o and lse.
  *
  * Rows with no valid key get dQ = 0; keys no row sees get dK = dV = 0.  Every

@@ -290,9 +290,12 @@ def call_bwd(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=136), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=12), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED),
     (dict(d=128, do=A + 8), fa.FA_ERR_ALIGN),      # d = 128 passes the head-dim check
+    (dict(d=32, do=A + 8), fa.FA_ERR_ALIGN),       # so do 32 and 96 (any multiple of 8 to 128)
+    (dict(d=96, do=A + 8), fa.FA_ERR_ALIGN),
     (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
     (dict(H_kv=3), fa.FA_ERR_SHAPE),
     (dict(Nq=-1), fa.FA_ERR_SHAPE),

@@ -140,6 +140,24 @@ def test_backward_d128_end_to_end():
     _check(w, _dout(w, 12951), "bwd d128 end-to-end", fwd="gpu")
 
 
+@pytest.mark.parametrize("d,H,Hkv,Nq,Nk,dtype,causal,lens", [
+    (8, 2, 2, 100, 100, "bf16", True, None),           # one 8-column group on the d = 64 tiles
+    (32, 4, 2, 161, 97, "f16", False, (40, 97)),       # grouped heads, padding
+    (48, 2, 1, 130, 200, "bf16", True, None),
+    (72, 2, 2, 97, 97, "bf16", True, None),            # just past 64: the d = 128 tiles
+    (96, 3, 3, 70, 150, "f16", True, (0, 150)),        # kv_len 0 in one batch
+    (120, 4, 1, 120, 64, "bf16", False, None),         # multi-query
+])
+def test_backward_head_dims(d, H, Hkv, Nq, Nk, dtype, causal, lens):
+    """Head dims other than 64 and 128, on the padded tiles: every gradient
+    element against the oracle (the columns past d are neither read nor
+    written)."""
+    w = gen.fwd_inputs(2, H, Nq, Nk, d, dtype, seed=13000 + d + Nq, causal=causal, kv_len_range=lens,
+                       Hkv=Hkv, scale=1.0 / math.sqrt(d))
+    _check(w, _dout(w, 13500 + d), f"bwd d{d} H{H}/{Hkv} Nq{Nq} Nk{Nk} {dtype} causal={causal} lens={lens}")
+    _check(w, _dout(w, 13600 + d), f"bwd d{d} end-to-end", fwd="gpu")
+
+
 @pytest.mark.parametrize("Nq,Nk", [(0, 70), (70, 0)])
 def test_backward_empty_side(Nq, Nk):
     """No query rows: dK = dV = 0 (no row sees the keys).  No keys: dQ = 0 and

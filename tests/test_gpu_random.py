@@ -8,7 +8,7 @@ batch, query and K/V heads (grouped-query and multi-query), Nq != Nk both
 ways, ragged tails, head dims 8..128, both 16-bit types, causal and key
 padding (including empty sequences), [B, N, H, d] views and 16-bit O for the
 forward; sequence counts, lengths from 0, head groups and both head dims for
-the decode; for the backward, both head dims it supports, grouped heads,
+the decode; for the backward, head dims 8..128, grouped heads,
 padding, both masks, and O/LSE from either the oracle or the GPU forward.
 Each case prints its parameters before it runs, so a failing draw names
 itself."""
@@ -113,7 +113,7 @@ def _bwd_case(seed):
     Nq = int(rng.integers(1, 400))
     Nk = Nq if rng.random() < 0.4 else int(rng.integers(1, 400))
     return dict(B=int(rng.integers(1, 3)), H=H, Hkv=Hkv, Nq=Nq, Nk=Nk,
-                d=int(rng.choice([64, 128])), dtype=str(rng.choice(["f16", "bf16"])),
+                d=8 * int(rng.integers(1, 17)), dtype=str(rng.choice(["f16", "bf16"])),
                 causal=bool(rng.random() < 0.5), padded=bool(rng.random() < 0.4),
                 fwd=str(rng.choice(["oracle", "gpu"])))
 
