@@ -138,3 +138,32 @@ def test_decode_deterministic(big):
     o1, l1 = run_decode(big, pools=pools)
     o2, l2 = run_decode(big, pools=pools)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_out_of_range_kv_lens_are_clamped():
+    """Decode kv_lens outside [0, max_pages * 16] act as their clamped values,
+    bitwise: a negative length is an empty sequence, a length past the page
+    table is the full table."""
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    inp = gen.decode_inputs(4, 8, 128, (100, 700), "bf16", seed=5900, page_size=16, num_pages=256, Hkv=2)
+    cap = inp.page_table.shape[1] * 16
+    kp = gen.build_pool_device(inp, "k", "cuda")
+    vp = gen.build_pool_device(inp, "v", "cuda")
+    q = gen.to_torch(inp.q, inp.dtype).cuda()
+    pt = torch.from_numpy(inp.page_table).cuda()
+
+    def run(lens):
+        kl = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+        o, lse = fa.decode_paged(q, kp, vp, pt, kl, scale=inp.scale)
+        torch.cuda.synchronize()
+        return o.cpu().numpy(), lse.cpu().numpy()
+
+    raw = [-5, cap + 37, int(inp.kv_lens[2]), 1 << 30]
+    o1, l1 = run(raw)
+    o2, l2 = run(np.clip(raw, 0, cap))
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), "O: kv_lens not clamped"
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32)), "LSE: kv_lens not clamped"
+    assert np.all(o1[0] == 0) and np.all(np.isneginf(l1[0])), "a negative length is an empty sequence"

@@ -135,3 +135,32 @@ def test_backward_ignores_poisoned_padding(B, H, Hkv, N, d, dtype, causal, lens)
         sel = np.isfinite(r)
         out[name] = compare_grad(x[sel], r[sel], f"poisoned bwd {name}")
     print(f"poisoned bwd d{d} {dtype} causal={causal} lens={lens}", out, flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_out_of_range_kv_lens_are_clamped(causal):
+    """kv_lens outside [0, Nk] act as their clamped values (negative: no key,
+    above Nk: every key), bitwise, in the forward and in the backward."""
+    import torch
+
+    import flashattention_forward_03_amd as fa
+
+    N = 150
+    w = _inputs(4, 2, 2, N, 64, "bf16", causal, (-7, N + 100, 97, 1 << 30), seed=13900 + causal)
+    clamped = np.clip(w.kv_lens, 0, N).astype(np.int32)
+    g = gen.to_torch(gen.round_bits(np.random.default_rng(13901).standard_normal(w.q.shape, dtype=np.float32),
+                                    "bf16"), "bf16").cuda()
+    q, k, v = (gen.to_torch(x, "bf16").cuda() for x in (w.q, w.k, w.v))
+
+    def run(lens):
+        kl = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+        o, lse = fa.forward(q, k, v, scale=w.scale, causal=causal, kv_lens=kl)
+        grads = fa.backward(q, k, v, o, lse, g, scale=w.scale, causal=causal, kv_lens=kl)
+        torch.cuda.synchronize()
+        return [x.cpu().numpy() for x in (o, lse, *grads)]
+
+    raw, ref = run(w.kv_lens), run(clamped)
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv", "delta"), raw, ref):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{name}: kv_lens not clamped"
+    o_ref, l_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, causal, clamped)
+    print(f"clamped kv_lens causal={causal}", compare(raw[0], raw[1], o_ref, l_ref, "clamped kv_lens"), flush=True)
