@@ -277,8 +277,9 @@ __device__ __forceinline__ void attend_qtile(
 // head; workgroups go to XCD blockIdx % 8, and when B*H is a multiple of 8
 // the heads are renumbered so that each XCD holds a contiguous range of them:
 // all tiles of a head, and the query heads that share a K/V head, then share
-// one XCD and its L2.  Non-causal: work ids are renumbered so that each XCD
-// receives a contiguous range.
+// one XCD and its L2.  For long sequences (many workgroups) the heads of an
+// XCD are further taken in groups, each group heaviest first.  Non-causal:
+// work ids are renumbered so that each XCD receives a contiguous range.
 // The causal flag is a runtime argument: both modes share one code path.
 template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd_kernel(
@@ -307,9 +308,21 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd
     int bhi, qt;
     if (causal) {
         const int BHn = gridDim.x / n_qtiles;
-        const int slot = blockIdx.x % BHn;
-        bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);
-        qt = n_qtiles - 1 - blockIdx.x / BHn;
+        // Long sequences: each XCD takes its heads in ng groups, one group's
+        // query tiles (heaviest first) after the other's, so that fewer heads'
+        // K/V rows compete for its L2; a group keeps at least 4096 workgroups
+        // (four rounds of the resident slots at d = 64), so that heaviest-first
+        // still balances inside it.
+        int ng = 1;
+        while (ng < 8 && BHn % (16 * ng) == 0 && (int)gridDim.x / (2 * ng) >= 4096)
+            ng *= 2;
+        const int per = gridDim.x / ng;   // workgroups of one group
+        const int grp = blockIdx.x / per;
+        const int r = blockIdx.x - grp * per;
+        const int BHg = BHn / ng;
+        const int slot = r % BHg;
+        bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + grp * (BHg >> 3) + (slot >> 3);
+        qt = n_qtiles - 1 - r / BHg;
     } else {
         const int logical = xcd_contiguous_id(blockIdx.x, gridDim.x);
         bhi = logical / n_units;
