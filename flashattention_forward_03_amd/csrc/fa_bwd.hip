@@ -48,6 +48,18 @@ constexpr int BK = 128;        // keys per dK/dV workgroup (32 per wave)
 constexpr int BT = 32;         // rows per streamed tile
 constexpr int STAGES = 3;      // LDS ring depth (tiles)
 
+// Head groups per XCD for a launch of `grid` workgroups over BHn heads: each
+// XCD's heads are taken one group after the other, so that fewer heads'
+// streamed rows compete for its L2, while every group keeps at least 3072
+// workgroups (four rounds of the 768 resident slots at d = 64).
+__device__ __forceinline__ int head_groups(int BHn, int grid)
+{
+    int ng = 1;
+    while (ng < 8 && BHn % (16 * ng) == 0 && grid / (2 * ng) >= 3072)
+        ng *= 2;
+    return ng;
+}
+
 // ---------------------------------------------------------------- dQ pass ---
 
 template <int D, bool BF16>
@@ -72,10 +84,16 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     const bool causal = causal_flag != 0;
 
     // heaviest query tiles first (as the forward), heads contiguous per XCD
+    // and, on long or wide launches, taken in groups per XCD
     const int BHn = gridDim.x / n_qtiles;
-    const int slot = blockIdx.x % BHn;
-    const int bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);
-    const int qt = causal ? n_qtiles - 1 - blockIdx.x / BHn : blockIdx.x / BHn;
+    const int ng = head_groups(BHn, gridDim.x);
+    const int per = gridDim.x / ng;
+    const int hgi = blockIdx.x / per;   // head group
+    const int rr = blockIdx.x - hgi * per;
+    const int BHg = BHn / ng;
+    const int slot = rr % BHg;
+    const int bhi = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + hgi * (BHg >> 3) + (slot >> 3);
+    const int qt = causal ? n_qtiles - 1 - rr / BHg : rr / BHg;
     const int b = bhi / H, h = bhi - b * H;
     const int kvh = h / (H / Hkv);
     int kvlen = Nk;
@@ -312,11 +330,17 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     const int hh = lane >> 5;
     const bool causal = causal_flag != 0;
 
-    // lowest key tiles first (they have the most query rows when causal)
+    // lowest key tiles first (they have the most query rows when causal),
+    // K/V heads contiguous per XCD and, on long or wide launches, in groups
     const int BHn = gridDim.x / n_ktiles;
-    const int slot = blockIdx.x % BHn;
-    const int g = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + (slot >> 3);   // b * Hkv + kvh
-    const int kt = blockIdx.x / BHn;
+    const int ng = head_groups(BHn, gridDim.x);
+    const int per = gridDim.x / ng;
+    const int hgi = blockIdx.x / per;   // head group
+    const int rr = blockIdx.x - hgi * per;
+    const int BHg = BHn / ng;
+    const int slot = rr % BHg;
+    const int g = (BHn & 7) ? slot : (slot & 7) * (BHn >> 3) + hgi * (BHg >> 3) + (slot >> 3);   // b * Hkv + kvh
+    const int kt = rr / BHg;
     const int b = g / Hkv, kvh = g - b * Hkv;
     const int grp = H / Hkv;
     const size_t n_rows = (size_t)(BHn / Hkv) * H * Nq;   // B * H * Nq: delta[1] starts here

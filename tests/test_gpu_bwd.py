@@ -158,6 +158,15 @@ def test_backward_head_dims(d, H, Hkv, Nq, Nk, dtype, causal, lens):
     _check(w, _dout(w, 13600 + d), f"bwd d{d} end-to-end", fwd="gpu")
 
 
+def test_backward_head_groups_of_a_long_launch():
+    """Both passes of a launch of 8192 workgroups (B256 H16 N256, causal, with
+    padding) take each XCD's heads in two groups; the oracle computes the full
+    gradients of heads from both groups and several XCDs."""
+    w = gen.fwd_inputs(256, 16, 256, 256, 64, "bf16", seed=13700, causal=True, kv_len_range=(1, 256))
+    _check(w, _dout(w, 13701), "bwd head groups B256 H16 N256", groups=[0, 1, 7, 8, 15, 16, 2047, 2048, 4095],
+           fwd="gpu")
+
+
 @pytest.mark.parametrize("Nq,Nk", [(0, 70), (70, 0)])
 def test_backward_empty_side(Nq, Nk):
     """No query rows: dK = dV = 0 (no row sees the keys).  No keys: dQ = 0 and

@@ -54,6 +54,17 @@ def test_workload_full_size_parity(name):
     print(name, "all", lse.size, "rows", stats, flush=True)
 
 
+def test_head_groups_of_a_long_launch():
+    """A causal launch of 8192 workgroups (B256 H16 N256: 4096 heads, 2 query
+    tiles each) takes each XCD's heads in two groups; every element against the
+    oracle, with padding so that the groups see different key counts."""
+    w = gen.fwd_inputs(256, 16, 256, 256, 64, "bf16", seed=9300, causal=True, kv_len_range=(1, 256))
+    o, lse = gpu_forward(w)
+    o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, w.kv_lens,
+                                          nthreads=host_cores())
+    print("head groups B256 H16 N256", compare(o, lse, o_ref, lse_ref, "head groups"), flush=True)
+
+
 # ------------------------------------------------ ragged and edge shapes
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,lens", [
