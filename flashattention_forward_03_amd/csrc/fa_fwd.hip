@@ -350,27 +350,27 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd
 // Small grids (few heads, short or single sequences): the tiled kernel above
 // gives each (b, h, 128-row query tile) to one workgroup, which leaves most
 // of the 256 CUs idle and makes every wave walk all keys of its rows in one
-// chain.  Here a workgroup owns one 32-row query block and its four waves
-// split the block's key tiles between them (tile t goes to wave t % 4), each
-// with its own two-slot LDS ring and no barrier in the loop; at the end the
-// four partial (O, m, l) are merged through LDS with the log-sum-exp rule, as
-// the split-KV decode merges its chunks (NanoInfer page "Online Softmax": the
-// same recurrence over blocks).
+// chain.  Here a workgroup owns one 32-row query block and its NW waves (4,
+// or 8 on the smallest grids at d <= 64) split the block's key tiles between
+// them (tile t goes to wave t % NW), each with its own two-slot LDS ring and
+// no barrier in the loop; at the end the NW partial (O, m, l) are merged
+// through LDS with the log-sum-exp rule, as the split-KV decode merges its
+// chunks (NanoInfer page "Online Softmax": the same recurrence over blocks).
 constexpr int SPLIT_ROWS = 32;
 constexpr int SPLIT_ST = 2;   // ring slots per wave
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
+template <int D, bool BF16, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_split_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     void *__restrict__ O, float *__restrict__ LSE, FwdLayout lay, int H, int Hkv, int Nq, int Nk, int n_qblocks,
     float c_log2, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
     constexpr int PPW = G::PIECES_PER_WAVE;
-    static_assert(4 * SPLIT_ST * 2 * G::TILE <= 160 * 1024, "LDS");
-    static_assert(4 * SPLIT_ROWS * D * 4 <= 4 * SPLIT_ST * 2 * G::TILE, "merge staging fits the rings");
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[4][SPLIT_ST][2][G::TILE];   // [wave][slot][K, V]
-    __shared__ float mls[2][4][SPLIT_ROWS];                                                   // m * c, l per wave
+    static_assert(NW * SPLIT_ST * 2 * G::TILE <= 160 * 1024, "LDS");
+    static_assert(NW * SPLIT_ROWS * D * 4 <= NW * SPLIT_ST * 2 * G::TILE, "merge staging fits the rings");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NW][SPLIT_ST][2][G::TILE];  // [wave][slot][K, V]
+    __shared__ float mls[2][NW][SPLIT_ROWS];                                                  // m * c, l per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
     int lim = kvlen;
     if (causal)
         lim = min(lim, qrow + dq + 1);
-    // this wave's tiles: t = wave, wave + 4, ...
-    const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
+    // this wave's tiles: t = wave, wave + NW, ...
+    const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
     f32x16_t oacc[G::DB];
 #pragma unroll
@@ -465,12 +465,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
     }
 
     for (int j = 0; j < my_tiles; ++j) {
-        const int t = wave + 4 * j;
+        const int t = wave + NW * j;
         const int slot = j & 1;
         // the other slot was read by this wave's previous tile (its MFMAs
         // consumed the reads), so it can be refilled now
         if (j + 1 < my_tiles) {
-            issue(t + 4, slot ^ 1);
+            issue(t + NW, slot ^ 1);
             wait_vmcnt<8 * PPW>();   // this tile's copies done, the next tile's in flight
         } else {
             wait_vmcnt<0>();
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
         pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
     }
 
-    // ---- merge of the four waves' partials: m*c and l per row, then O
+    // ---- merge of the NW waves' partials: m*c and l per row, then O
     const float l_tot = st.l + other_half(st.l);
     __syncthreads();   // every wave is done with its ring: it becomes the staging area
     if (hh == 0) {
@@ -505,15 +505,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
             *reinterpret_cast<f32x4_t *>(stage + (((wave * G::DB + db) * 4 + g) * 64 + lane) * 4) =
                 f32x4_t{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
     __syncthreads();
-    float mw[4], M = -INFINITY;
+    float mw[NW], M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
         mw[w] = mls[0][w][l32];
         M = fmaxf(M, mw[w]);
     }
-    float fw[4], L = 0.f;
+    float fw[NW], L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
         fw[w] = M == -INFINITY ? 0.f : fast_exp2(mw[w] - M);   // a wave without keys of this row: mw = -inf, weight 0
         L = fmaf(fw[w], mls[1][w][l32], L);
     }
@@ -521,16 +521,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_split_kernel(
     if (qrow < Nq) {
         void *orow = lay.o_kind == FA_O_F32 ? (void *)(static_cast<float *>(O) + oe + qrow * lay.os[2])
                                             : (void *)(static_cast<uint16_t *>(O) + oe + qrow * lay.os[2]);
-        // wave w merges and stores the (db, g) groups with (4 db + g) % 4 == w
+        // wave w merges and stores the (db, g) groups with (4 db + g) % NW == w
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                if (g != wave)
+                if ((4 * db + g) % NW != wave)
                     continue;
                 f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int w = 0; w < 4; ++w)
+                for (int w = 0; w < NW; ++w)
                     acc += fw[w] * *reinterpret_cast<const f32x4_t *>(stage + (((w * G::DB + db) * 4 + g) * 64 + lane) * 4);
                 const int dim0 = 32 * db + 8 * g + 4 * hh;
                 if (dim0 < d)
@@ -550,36 +550,53 @@ int units_per_head(int Nq, bool causal)
 
 // Kernel choice: the split-key kernel when the tiled kernel would launch
 // fewer workgroups than the GPU has CUs (d = 96 excepted: its two-slot rings
-// per wave would not fit in LDS).  FA_FWD_SPLIT=0 / 1 in the environment
-// forces the tiled / split kernel (the tests run both on the same shapes).
-bool use_split(const FwdArgs &a, int D)
+// per wave would not fit in LDS), with 8 waves per 32-row block when even
+// that grid (four blocks per query tile) fits one workgroup per CU at d <= 64
+// (the rings of 8 waves take 128 KB of LDS).  Returns the split kernel's
+// waves per workgroup, or 0 for the tiled kernel.  FA_FWD_SPLIT=0 / 1 / 8 in
+// the environment forces the tiled kernel / 4 waves / 8 waves (4 above d = 64);
+// the tests run every kernel on the same shapes.
+int split_waves(const FwdArgs &a, int D)
 {
     if (D == 96)
-        return false;
+        return 0;
     const long long tiled = (long long)((a.Nq + BM - 1) / BM) * a.B * a.H;
     if (tiled >= (1 << 20))   // keep the split grid (4x) far inside the 32-bit grid limit
-        return false;
+        return 0;
     const char *e = std::getenv("FA_FWD_SPLIT");
     if (e && e[0] == '0' && e[1] == 0)
-        return false;
+        return 0;
     if (e && e[0] == '1' && e[1] == 0)
-        return true;
-    return tiled < 256;
+        return 4;
+    if (e && e[0] == '8' && e[1] == 0)
+        return D <= 64 ? 8 : 4;
+    if (tiled <= 64 && D <= 64)
+        return 8;
+    return tiled < 256 ? 4 : 0;
+}
+
+template <int D, bool BF16, int NW>
+hipError_t launch_split(const FwdArgs &a, hipStream_t stream)
+{
+    const int n_qblocks = (a.Nq + SPLIT_ROWS - 1) / SPLIT_ROWS;
+    const long long grid = (long long)n_qblocks * a.B * a.H;
+    hipLaunchKernelGGL((fwd_split_kernel<D, BF16, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse, a.lay,
+                       a.H, a.Hkv, a.Nq, a.Nk, n_qblocks, a.scale * kLog2e, a.causal ? 1 : 0, a.kv_lens);
+    return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
     if constexpr (D != 96) {
-        if (use_split(a, D)) {
-            const int n_qblocks = (a.Nq + SPLIT_ROWS - 1) / SPLIT_ROWS;
-            const long long grid = (long long)n_qblocks * a.B * a.H;
-            hipLaunchKernelGGL((fwd_split_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
-                               (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse,
-                               a.lay, a.H, a.Hkv, a.Nq, a.Nk, n_qblocks, a.scale * kLog2e, a.causal ? 1 : 0,
-                               a.kv_lens);
-            return hipGetLastError();
+        const int nw = split_waves(a, D);
+        if constexpr (D <= 64) {
+            if (nw == 8)
+                return launch_split<D, BF16, 8>(a, stream);
         }
+        if (nw != 0)
+            return launch_split<D, BF16, 4>(a, stream);
     }
     const int n_qtiles = (a.Nq + BM - 1) / BM;
     const int n_units = units_per_head(a.Nq, a.causal);
@@ -593,8 +610,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
 
 }  // namespace
 
-// upper bound of the tiled kernel's grid; the split-key kernel only runs when
-// that grid is below 256, so its own (4x) grid stays below 1024
+// upper bound of the tiled kernel's grid; the split-key kernel's grid is 4x
+// this, and split_waves() keeps it for tiled grids below 2^20 only
 long long fwd_grid_size(int B, int H, int Nq) { return (long long)((Nq + BM - 1) / BM) * B * H; }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)

@@ -104,9 +104,11 @@ extern "C" {
  * and, when that would launch fewer than 256 workgroups (few heads, short or
  * single sequences) and d > 96 or d <= 64, a split-key one (a workgroup per
  * 32-row block whose four waves share out its keys and merge their partial
- * results by the log-sum-exp rule).  Both give the same result up to rounding
- * order.  The environment variable FA_FWD_SPLIT=0 or 1, read at each call,
- * forces the tiled or the split-key kernel (for testing either on any shape).
+ * results by the log-sum-exp rule; eight waves when the tiled grid would be at
+ * most 64 workgroups and d <= 64).  All give the same result up to rounding
+ * order.  The environment variable FA_FWD_SPLIT=0, 1 or 8, read at each call,
+ * forces the tiled kernel or the split-key kernel with four or eight waves (for
+ * testing each on any shape; eight becomes four above d = 64).
  */
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H,
            int Nq, int Nk, int d, float scale, int causal, const int32_t *kv_lens, int dtype,

@@ -50,13 +50,13 @@ def test_side_stream_gives_the_default_stream_bits():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kernel", ["tiled", "split"])
+@pytest.mark.parametrize("kernel", ["tiled", "split", "split8"])
 def test_graph_capture_replays_match_eager_runs(kernel, monkeypatch):
     import torch
 
     import flashattention_forward_03_amd as fa
 
-    monkeypatch.setenv("FA_FWD_SPLIT", "0" if kernel == "tiled" else "1")
+    monkeypatch.setenv("FA_FWD_SPLIT", {"tiled": "0", "split": "1", "split8": "8"}[kernel])
     w = _fwd_inputs(15100)
     q, k, v = _dev(w)
     B, H, N, d = q.shape
