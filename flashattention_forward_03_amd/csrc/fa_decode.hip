@@ -177,9 +177,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(
         if (tok0 + G::BN > kvlen)
             mask_tile<D>(sc, kvlen - (tok0 + 8 * hh));
         u32x4_t pf[G::PCH];
-        float alpha;
-        if (__builtin_expect(softmax_tile<D, BF16>(sc, st, pf, c_log2, tau_log2, alpha), 0))
-            rescale_acc<D>(oacc, alpha);
+        softmax_tile<D, BF16>(sc, st, pf, c_log2, tau_log2, oacc);
         pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
     }
 

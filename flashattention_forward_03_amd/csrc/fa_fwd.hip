@@ -93,7 +93,7 @@ __device__ __forceinline__ void attend_qtile(
         wave_key_end = min(wave_key_end, max(wlast + dq + 1, 0));
     }
     constexpr int BN = G::BN;
-    const int n_tiles = (key_end + BN - 1) / BN;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((key_end + BN - 1) / BN);
     const int wave_tiles = min(n_tiles, (wave_key_end + BN - 1) / BN);
 
     // first tile that needs the mask (both conditions only grow with t): the
@@ -205,9 +205,7 @@ __device__ __forceinline__ void attend_qtile(
             if (!fast && t >= mask_t)
                 mask_tile<D>(s, lim - (kt0 + 8 * hh));
             u32x4_t pf[G::PCH];
-            float alpha;
-            if (__builtin_expect(softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha), 0))
-                rescale_acc<D>(oacc, alpha);
+            softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, oacc);
             // keep the V operand reads after the softmax (register pressure)
             __builtin_amdgcn_sched_barrier(0);
             pv_tile<D, BF16>(vbuf[cur], lane, hh, pf, oacc);
@@ -218,7 +216,7 @@ __device__ __forceinline__ void attend_qtile(
     // passes one barrier per tile, whichever loop it is in.
     const LoopTag<true> F;
     const LoopTag<false> C;
-    const int fast_end = min(min(n_tiles - (ST - 1), wave_tiles), mask_t);
+    const int fast_end = __builtin_amdgcn_readfirstlane(min(min(n_tiles - (ST - 1), wave_tiles), mask_t));
     int t = 0;
     if constexpr (ST == 3) {
         for (; t + 2 < fast_end; t += 3) {
@@ -310,11 +308,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd
         const int BHn = gridDim.x / n_qtiles;
         // Long sequences: each XCD takes its heads in ng groups, one group's
         // query tiles (heaviest first) after the other's, so that fewer heads'
-        // K/V rows compete for its L2; a group keeps at least 4096 workgroups
-        // (four rounds of the resident slots at d = 64), so that heaviest-first
+        // K/V rows compete for its L2; a group keeps at least 2048 workgroups
+        // (two rounds of the resident slots at d = 64), so that heaviest-first
         // still balances inside it.
         int ng = 1;
-        while (ng < 8 && BHn % (16 * ng) == 0 && (int)gridDim.x / (2 * ng) >= 4096)
+        while (ng < 8 && BHn % (16 * ng) == 0 && (int)gridDim.x / (2 * ng) >= 2048)
             ng *= 2;
         const int per = gridDim.x / ng;   // workgroups of one group
         const int grp = blockIdx.x / per;
@@ -404,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_split_kernel(
     int key_end = kvlen;
     if (causal)
         key_end = min(key_end, max(min(q0 + SPLIT_ROWS, Nq) - 1 + dq + 1, 0));
-    const int n_tiles = (key_end + BN - 1) / BN;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((key_end + BN - 1) / BN);
     int mask_t = kvlen / BN;   // first tile that needs the mask
     if (causal) {
         const int x1 = q0 + dq + 1;
@@ -484,9 +482,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_split_kernel(
         if (t >= mask_t)
             mask_tile<D>(s, lim - (t * BN + 8 * hh));
         u32x4_t pf[G::PCH];
-        float alpha;
-        if (__builtin_expect(softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, alpha), 0))
-            rescale_acc<D>(oacc, alpha);
+        softmax_tile<D, BF16>(s, st, pf, c_log2, tau_log2, oacc);
         pv_tile<D, BF16>(vc, lane, hh, pf, oacc);
     }
 

@@ -348,6 +348,14 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
+template <int D>
+__device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alpha)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+        oacc[db] *= alpha;
+}
+
 // Online softmax step for one tile.  The running max m only has to keep
 // p = exp2(s*c - m*c) below 2^tau (no overflow in the 16-bit P, fp32 sums),
 // and the exact softmax does not depend on which m is used (m cancels in
@@ -355,19 +363,18 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
 // compute the tile max at all: it forms p against the current m and checks
 // the row sum (sum >= max p); only when some row of the wave exceeds 2^tau,
 // overflowed, or has no finite m yet (its first keys) does the wave take
-// the exact path: tile max, new m = max(m, tile max), rescale of l and O by
-// alpha = exp2((m_old - m_new) * c), p recomputed.  Returns true (wave-
-// uniform) when O must be multiplied by alpha (done by the caller).  The
-// no-finite-m case needs no compare of its own: mc is -inf then, which makes
-// the row sum +inf or NaN.
+// the exact path: tile max, new m = max(m, tile max), l and the O
+// accumulators scaled by alpha = exp2((m_old - m_new) * c), p recomputed.
+// The no-finite-m case needs no compare of its own: mc is -inf then, which
+// makes the row sum +inf or NaN.  Every scaling by alpha stays inside the
+// exact path, so the common path carries no alpha at all: its l update is
+// one add.
 template <int D, bool BF16>
-__device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
+__device__ __forceinline__ void softmax_tile(const f32x16_t (&s)[kBN<D> / 32], RowState &st,
                                              u32x4_t (&pf)[kBN<D> / 16], float c_log2, float tau_log2,
-                                             float &alpha)
+                                             f32x16_t (&oacc)[D / 32])
 {
     const float limit = exp2f(tau_log2);
-    alpha = 1.f;
-    bool rescale = false;
     // While m is -inf, mc is -inf too, so p = exp2(s*c + inf) is +inf (or
     // NaN for a masked score) and the one compare below sends the row to the
     // exact path; the exact path is marked unlikely for the code layout.
@@ -384,23 +391,16 @@ __device__ __forceinline__ bool softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
         mx = fmaxf(mx, other_half(mx));
         const float m_new = fmaxf(st.m, mx);
         // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
-        alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
         st.m = m_new;
         st.mc = m_new * c_log2;
-        rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+        st.l *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0)
+            rescale_acc<D>(oacc, alpha);
         // (a row with no key yet: p = exp2(-inf - 0) = 0)
         psum = exp_tile<kBN<D> / 32, BF16>(s, m_new == -INFINITY ? 0.f : st.mc, c_log2, pf);
     }
-    st.l = fmaf(st.l, alpha, psum);
-    return rescale;
-}
-
-template <int D>
-__device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alpha)
-{
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-        oacc[db] *= alpha;
+    st.l += psum;
 }
 
 // Compile-time flag for a tile loop's iteration: true for the check-free
