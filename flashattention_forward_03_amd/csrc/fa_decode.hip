@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    RowState st{-INFINITY, 0.f, -INFINITY};
+    RowState st{INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     const int krow_in_blk = sigma(l32);
     // SLOTS - 1 sub-tiles in flight ahead of the one being computed; a slot is
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(
 
     // this slice's partial (or final) rows: query head h0 + l32 in both halves
     const float L = st.l + other_half(st.l);
-    const float M = st.m == -INFINITY ? 0.f : st.mc;   // running max in base-2 units (m * c)
+    const float M = st.nmc == INFINITY ? 0.f : -st.nmc;   // running max in base-2 units (m * c)
     if (l32 >= nq)
         return;
     const size_t sh = (size_t)s * H + h0 + l32;

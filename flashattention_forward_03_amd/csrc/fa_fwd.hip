@@ -74,7 +74,7 @@ __device__ __forceinline__ void attend_qtile(
     const uint16_t *__restrict__ Qb, long long qsn, const uint16_t *__restrict__ Kb, unsigned krs,
     const uint16_t *__restrict__ Vb, unsigned vrs, void *__restrict__ Ob, long long osn, int o_kind,
     float *__restrict__ LSEb, int d, int Nq, int Nk, int kvlen, int q0,
-    float c_log2, float scale, bool causal, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
+    float c_log2, bool causal, unsigned char *const (&kbuf)[Pipe<D>::STAGES],
     unsigned char *const (&vbuf)[Pipe<D>::STAGES], int wave, int lane)
 {
     using G = Geometry<D>;
@@ -113,7 +113,7 @@ __device__ __forceinline__ void attend_qtile(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    RowState st{-INFINITY, 0.f, -INFINITY};
+    RowState st{INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     int ko[G::NBLK][G::KSTEPS];   // K operand read offsets inside a tile
     qk_offsets<D>(sigma(l32), hh, ko);
@@ -248,7 +248,7 @@ __device__ __forceinline__ void attend_qtile(
     __syncthreads();   // the ring is reused by the next query tile of this workgroup
 
     // ---- epilogue: O = O_acc / l (columns < d, in the output type),
-    // LSE = m * scale + ln(l)
+    // LSE = m * scale + ln(l) = (m*c + log2(l)) * ln(2)
     const float l_tot = st.l + other_half(st.l);
     if (qrow < Nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -264,7 +264,7 @@ __device__ __forceinline__ void attend_qtile(
                              oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
             }
         if (hh == 0)
-            LSEb[qrow] = l_tot > 0.f ? st.m * scale + __log2f(l_tot) * kLn2 : -INFINITY;
+            LSEb[qrow] = l_tot > 0.f ? (__log2f(l_tot) - st.nmc) * kLn2 : -INFINITY;
     }
 }
 
@@ -283,7 +283,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     void *__restrict__ O, float *__restrict__ LSE, FwdLayout lay, int H, int Hkv, int Nq, int Nk, int n_qtiles,
-    int n_units, float c_log2, float scale, int causal_flag, const int32_t *__restrict__ kv_lens)
+    int n_units, float c_log2, int causal_flag, const int32_t *__restrict__ kv_lens)
 {
     using G = Geometry<D>;
     constexpr int ST = Pipe<D>::STAGES;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 4 : (D == 96 ? 2 : 3)) void fwd
     void *Ob = lay.o_kind == FA_O_F32 ? (void *)(static_cast<float *>(O) + oe) : (void *)(static_cast<uint16_t *>(O) + oe);
 
     attend_qtile<D, BF16>(Qb, lay.qs[2], Kb, (unsigned)(lay.ks[2] * 2), Vb, (unsigned)(lay.vs[2] * 2), Ob, lay.os[2],
-                          lay.o_kind, LSE + (size_t)bhi * Nq, lay.d, Nq, Nk, kvlen, qt * BM, c_log2, scale, causal,
+                          lay.o_kind, LSE + (size_t)bhi * Nq, lay.d, Nq, Nk, kvlen, qt * BM, c_log2, causal,
                           kbuf, vbuf, wave, lane);
 }
 
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_split_kernel(
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         oacc[db] = f32x16_t{};
-    RowState st{-INFINITY, 0.f, -INFINITY};
+    RowState st{INFINITY, 0.f};
     const float tau_log2 = kRescaleLog2<BF16>;
     int ko[G::NBLK][G::KSTEPS];
     qk_offsets<D>(sigma(l32), hh, ko);
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_split_kernel(
     const float l_tot = st.l + other_half(st.l);
     __syncthreads();   // every wave is done with its ring: it becomes the staging area
     if (hh == 0) {
-        mls[0][wave][l32] = st.mc;
+        mls[0][wave][l32] = -st.nmc;   // m*c (-inf: no key)
         mls[1][wave][l32] = l_tot;
     }
     float *stage = reinterpret_cast<float *>(&ring[0][0][0][0]);   // [wave][db][g][lane] f32x4
@@ -599,7 +599,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     const long long grid = (long long)n_units * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, BF16>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o, a.lse, a.lay,
-                       a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.scale, a.causal ? 1 : 0,
+                       a.H, a.Hkv, a.Nq, a.Nk, n_qtiles, n_units, a.scale * kLog2e, a.causal ? 1 : 0,
                        a.kv_lens);
     return hipGetLastError();
 }

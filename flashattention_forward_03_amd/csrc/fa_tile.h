@@ -318,18 +318,20 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[kBN<D> / 32], int rel)
 // exponent (log2) units: f16 P must stay below 65504, bf16 has fp32's range.
 template <bool BF16>
 constexpr float kRescaleLog2 = BF16 ? 32.0f : 15.0f;
-// Per-lane online-softmax state.
+// Per-lane online-softmax state.  The running max m is kept only in base-2
+// units and negated, nmc = -m*c (c = scale*log2(e) > 0), which is what each
+// probability p = exp2(s*c + nmc) adds; nmc is +inf until a key is seen.
 struct RowState {
-    float m;    // running max, raw score units (-inf until a key is seen)
-    float l;    // running sum of exp2(s*c - m*c), fp32
-    float mc;   // m*c, or -inf while m is -inf (kept, not recomputed per tile)
+    float nmc;   // -m*c
+    float l;     // running sum of exp2(s*c + nmc), fp32
 };
 
 // Probabilities of one tile against the row's current (possibly stale) max
-// m: p = exp2(s*c - m*c), packed to 16 bits for the MFMA, summed in fp32
-// (4 independent partial sums).  Returns the row sum of this lane's 32 p.
+// m: p = exp2(s*c + nmc) with nmc = -m*c, packed to 16 bits for the MFMA,
+// summed in fp32 (4 independent partial sums).  Returns the row sum of this
+// lane's 32 p.
 template <int NB, bool BF16>
-__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, float c_log2, u32x4_t (&pf)[2 * NB])
+__device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float nmc, float c_log2, u32x4_t (&pf)[2 * NB])
 {
     float ps[4];
 #pragma unroll
@@ -339,8 +341,8 @@ __device__ __forceinline__ float exp_tile(const f32x16_t (&s)[NB], float mc, flo
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = 8 * h2 + 2 * q;
-                const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, -mc));
-                const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, -mc));
+                const float p0 = fast_exp2(fmaf(s[blk][r], c_log2, nmc));
+                const float p1 = fast_exp2(fmaf(s[blk][r + 1], c_log2, nmc));
                 pf[2 * blk + h2][q] = pack2<BF16>(p0, p1);
                 // the first pair starts each partial sum (no 0 + x: x may be -0)
                 ps[q] = (blk == 0 && h2 == 0) ? p0 + p1 : ps[q] + (p0 + p1);
@@ -375,10 +377,10 @@ __device__ __forceinline__ void softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
                                              f32x16_t (&oacc)[D / 32])
 {
     const float limit = exp2f(tau_log2);
-    // While m is -inf, mc is -inf too, so p = exp2(s*c + inf) is +inf (or
-    // NaN for a masked score) and the one compare below sends the row to the
+    // While m is -inf, nmc is +inf, so p = exp2(s*c + inf) is +inf (or NaN
+    // for a masked score) and the one compare below sends the row to the
     // exact path; the exact path is marked unlikely for the code layout.
-    float psum = exp_tile<kBN<D> / 32, BF16>(s, st.mc, c_log2, pf);
+    float psum = exp_tile<kBN<D> / 32, BF16>(s, st.nmc, c_log2, pf);
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(psum <= limit)) != 0, 0)) {
         // exact path: tile max (lane-local, then the other half of the wave),
         // then p again against the new max (p <= 1)
@@ -389,16 +391,20 @@ __device__ __forceinline__ void softmax_tile(const f32x16_t (&s)[kBN<D> / 32], R
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[blk][r]);
         mx = fmaxf(mx, other_half(mx));
-        const float m_new = fmaxf(st.m, mx);
-        // 0 when m was -inf and is now finite; 1 when still -inf (O and l are 0)
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((st.m - m_new) * c_log2);
-        st.m = m_new;
-        st.mc = m_new * c_log2;
+        // new max in the same units: nmc = -max(m, mx)*c (c > 0, so the max
+        // commutes with the scaling), updated in place after the old value's
+        // last use, and alpha = exp2((m_old - m_new)*c) = exp2(min(dx, 0))
+        // with dx = -mx*c - nmc_old: 0 when m was -inf and is now finite; 1
+        // when m is still -inf (O and l are 0)
+        const float nx = -(mx * c_log2);
+        const float dx = nx - st.nmc;
+        st.nmc = fminf(st.nmc, nx);
+        const float alpha = (st.nmc == INFINITY) ? 1.f : fast_exp2(fminf(dx, 0.f));
         st.l *= alpha;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0)
             rescale_acc<D>(oacc, alpha);
-        // (a row with no key yet: p = exp2(-inf - 0) = 0)
-        psum = exp_tile<kBN<D> / 32, BF16>(s, m_new == -INFINITY ? 0.f : st.mc, c_log2, pf);
+        // (a row with no key yet: p = exp2(-inf + 0) = 0)
+        psum = exp_tile<kBN<D> / 32, BF16>(s, st.nmc == INFINITY ? 0.f : st.nmc, c_log2, pf);
     }
     st.l += psum;
 }
