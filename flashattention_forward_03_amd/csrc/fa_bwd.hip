@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
         key_end = min(key_end, max(min(q0 + BQ, Nq) - 1 + dq + 1, 0));
         wave_key_end = min(wave_key_end, max(min(wave_first_row + 32, Nq) - 1 + dq + 1, 0));
     }
-    const int n_tiles = (key_end + BT - 1) / BT;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((key_end + BT - 1) / BT);
     const int wave_tiles = min(n_tiles, (wave_key_end + BT - 1) / BT);
     const int qrow = wave_first_row + l32;
     int lim = kvlen;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 2) void bwd_dq_kernel(
     };
     const LoopTag<true> F;
     const LoopTag<false> C;
-    const int fast_end = min(min(n_tiles - (STAGES - 1), wave_tiles), mask_t);
+    const int fast_end = __builtin_amdgcn_readfirstlane(min(min(n_tiles - (STAGES - 1), wave_tiles), mask_t));
     int t = 0;
     for (; t + 2 < fast_end; t += 3) {
         iter(t, 0, 2, F);
@@ -308,6 +308,48 @@ __device__ __forceinline__ void dma_dword_lds(const u32x4s_t &rsrc, unsigned vof
                  : "memory", "m0");
 }
 
+// pv_operands in two halves: the per-lane byte offsets of its transposing
+// reads inside a tile (loop-invariant), then the reads at a tile's base.
+template <int D, bool KSWZ = false>
+__device__ __forceinline__ void pv_offsets(int lane, int hh, int (&to)[D / 32][kBN<D> / 16][2])
+{
+    using G = Geometry<D>;
+    const int j16 = lane & 15;
+    const int g16 = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        const int col = 32 * db + 16 * (g16 & 1) + 4 * (j16 & 3);
+        const int chunk = col >> 3;
+        const int half = (col & 7) * 2;
+#pragma unroll
+        for (int c = 0; c < G::PCH; ++c) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 16 * c + 8 * hh + (j16 >> 2) + 4 * e;
+                const int sw = KSWZ ? swz_k(r) : swz_v(r);
+                to[db][c][e] = r * G::ROWB + (swz_slot<G::DC>(chunk, sw) << 4) + half;
+            }
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_read(const unsigned char *vb, const int (&to)[D / 32][kBN<D> / 16][2],
+                                        u32x4_t (&va)[D / 32][kBN<D> / 16])
+{
+    using G = Geometry<D>;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int c = 0; c < G::PCH; ++c) {
+            const u32x2_t y0 = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + to[db][c][0])));
+            const u32x2_t y1 = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + to[db][c][1])));
+            va[db][c] = u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+        }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -319,8 +361,9 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     const unsigned rb = (unsigned)d * 2u;   // bytes per Q/dO row in memory
     static_assert(G::BN == BT, "tile rows");
     constexpr int PER = 2 * G::PIECES_PER_WAVE + 2;   // Q, dO pieces + LSE, D rows
-    __shared__ __attribute__((aligned(1024))) unsigned char qring[STAGES][G::TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char gring[STAGES][G::TILE];
+    // Q and dO tiles of one ring slot side by side, so that one lane offset
+    // (plus a constant) addresses both
+    __shared__ __attribute__((aligned(1024))) unsigned char qgring[STAGES][2][G::TILE];
     __shared__ __attribute__((aligned(256))) unsigned char sring[STAGES][4][2][256];   // per wave: LSE, D
 
     const int tid = threadIdx.x;
@@ -388,8 +431,8 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
     uint32_t qlds[STAGES], glds[STAGES], llds[STAGES], dlds[STAGES];
 #pragma unroll
     for (int i = 0; i < STAGES; ++i) {
-        qlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(qring[i] + wave * 1024));
-        glds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(gring[i] + wave * 1024));
+        qlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(qgring[i][0] + wave * 1024));
+        glds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(qgring[i][1] + wave * 1024));
         llds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)sring[i][wave][0]);
         dlds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)sring[i][wave][1]);
     }
@@ -444,6 +487,10 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
         dvacc[db] = f32x16_t{};
     }
     const int qrow_perm = sigma(l32);
+    int ro[1][G::KSTEPS];   // row-read offsets of the Q / dO operands inside a tile
+    qk_offsets<D>(qrow_perm, hh, ro);
+    int to[G::DB][G::PCH][2];   // transposing-read offsets of Q^T / dO^T inside a tile
+    pv_offsets<D, true>(lane, hh, to);
     const int lim_key = min(kvlen, Nk);
     // rows this lane's key is visible to: [row_lo, Nq), none past the key range
     const int row_lo = key >= lim_key ? INT_MAX : (causal ? key - dq : INT_MIN);
@@ -475,8 +522,13 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
                 for (int e = 0; e < 8; ++e)
                     dp[0][8 * h2 + e] = e < 4 ? da[e] : dbv[e - 4];
             }
-            qk_tile<D, BF16>(qring[cur], qrow_perm, hh, kf, s);            // S = Q K^T
-            qk_tile_acc<D, BF16>(gring[cur], qrow_perm, hh, vf, dp);       // D - dP = D + dO (-V)^T
+            u32x4_t qa[1][G::KSTEPS], ga[1][G::KSTEPS];
+            qk_read<D>(qgring[cur][0], ro, qa);
+            qk_read<D>(qgring[cur][1], ro, ga);
+            qk_mma<D, BF16>(qa, kf, s);                        // S = Q K^T
+#pragma unroll
+            for (int c = 0; c < G::KSTEPS; ++c)
+                dp[0] = mma32<BF16>(ga[0][c], vf[c], dp[0]);   // D - dP = D + dO (-V)^T
             __builtin_amdgcn_sched_barrier(0);
             // P, and -dS = P (D - dP)
             float p[16], dsv[16];
@@ -513,11 +565,11 @@ __global__ __launch_bounds__(NTHREADS, D == 64 ? 3 : 1) void bwd_dkdv_kernel(
                 }
             __builtin_amdgcn_sched_barrier(0);
             u32x4_t ta[G::DB][G::PCH];
-            pv_operands<D, true>(gring[cur], lane, hh, ta);   // dO^T
-            pv_mfma<D, BF16>(ta, pf, dvacc);                  // dV^T += dO^T P
+            pv_read<D>(qgring[cur][1], to, ta);   // dO^T
+            pv_mfma<D, BF16>(ta, pf, dvacc);      // dV^T += dO^T P
             __builtin_amdgcn_sched_barrier(0);
-            pv_operands<D, true>(qring[cur], lane, hh, ta);   // Q^T
-            pv_mfma<D, BF16>(ta, dsf, dkacc);                 // (-dK)^T += Q^T (-dS)
+            pv_read<D>(qgring[cur][0], to, ta);   // Q^T
+            pv_mfma<D, BF16>(ta, dsf, dkacc);     // (-dK)^T += Q^T (-dS)
         }
     };
     int t = 0;
