@@ -367,7 +367,7 @@ __device__ __forceinline__ void rescale_acc(f32x16_t (&oacc)[D / 32], float alph
 // overflowed, or has no finite m yet (its first keys) does the wave take
 // the exact path: tile max, new m = max(m, tile max), l and the O
 // accumulators scaled by alpha = exp2((m_old - m_new) * c), p recomputed.
-// The no-finite-m case needs no compare of its own: mc is -inf then, which
+// The no-finite-m case needs no compare of its own: nmc is +inf then, which
 // makes the row sum +inf or NaN.  Every scaling by alpha stays inside the
 // exact path, so the common path carries no alpha at all: its l update is
 // one add.
