@@ -50,12 +50,12 @@ constexpr int STAGES = 3;      // LDS ring depth (tiles)
 
 // Head groups per XCD for a launch of `grid` workgroups over BHn heads: each
 // XCD's heads are taken one group after the other, so that fewer heads'
-// streamed rows compete for its L2, while every group keeps at least 3072
-// workgroups (four rounds of the 768 resident slots at d = 64).
+// streamed rows compete for its L2, while every group keeps at least 2048
+// workgroups (more than two rounds of the 768 resident slots at d = 64).
 __device__ __forceinline__ int head_groups(int BHn, int grid)
 {
     int ng = 1;
-    while (ng < 8 && BHn % (16 * ng) == 0 && grid / (2 * ng) >= 3072)
+    while (ng < 8 && BHn % (16 * ng) == 0 && grid / (2 * ng) >= 2048)
         ng *= 2;
     return ng;
 }

@@ -160,8 +160,8 @@ def test_backward_head_dims(d, H, Hkv, Nq, Nk, dtype, causal, lens):
 
 def test_backward_head_groups_of_a_long_launch():
     """Both passes of a launch of 8192 workgroups (B256 H16 N256, causal, with
-    padding) take each XCD's heads in two groups; the oracle computes the full
-    gradients of heads from both groups and several XCDs."""
+    padding) take each XCD's heads in four groups; the oracle computes the full
+    gradients of heads from several groups and XCDs."""
     w = gen.fwd_inputs(256, 16, 256, 256, 64, "bf16", seed=13700, causal=True, kv_len_range=(1, 256))
     _check(w, _dout(w, 13701), "bwd head groups B256 H16 N256", groups=[0, 1, 7, 8, 15, 16, 2047, 2048, 4095],
            fwd="gpu")

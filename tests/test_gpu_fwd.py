@@ -56,7 +56,7 @@ def test_workload_full_size_parity(name):
 
 def test_head_groups_of_a_long_launch():
     """A causal launch of 8192 workgroups (B256 H16 N256: 4096 heads, 2 query
-    tiles each) takes each XCD's heads in two groups; every element against the
+    tiles each) takes each XCD's heads in four groups; every element against the
     oracle, with padding so that the groups see different key counts."""
     w = gen.fwd_inputs(256, 16, 256, 256, 64, "bf16", seed=9300, causal=True, kv_len_range=(1, 256))
     o, lse = gpu_forward(w)
