@@ -167,6 +167,15 @@ def test_backward_head_groups_of_a_long_launch():
            fwd="gpu")
 
 
+def test_backward_eight_head_groups():
+    """Both passes of a launch of 16384 workgroups (B512 H16 N256, causal, with
+    padding) take each XCD's heads in eight groups; full gradients of K/V heads
+    from the first, second and last groups of two XCDs and from the middle."""
+    w = gen.fwd_inputs(512, 16, 256, 256, 64, "bf16", seed=13710, causal=True, kv_len_range=(1, 256))
+    _check(w, _dout(w, 13711), "bwd eight head groups B512 H16 N256",
+           groups=[0, 127, 128, 1023, 1024, 5000, 8191], fwd="gpu")
+
+
 @pytest.mark.parametrize("Nq,Nk", [(0, 70), (70, 0)])
 def test_backward_empty_side(Nq, Nk):
     """No query rows: dK = dV = 0 (no row sees the keys).  No keys: dQ = 0 and

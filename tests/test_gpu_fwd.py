@@ -65,6 +65,17 @@ def test_head_groups_of_a_long_launch():
     print("head groups B256 H16 N256", compare(o, lse, o_ref, lse_ref, "head groups"), flush=True)
 
 
+def test_eight_head_groups_of_a_long_launch():
+    """A causal launch of 16384 workgroups (B512 H16 N256: 8192 heads) takes
+    each XCD's heads in eight groups, the most the mapping makes; every element
+    against the oracle, with padding."""
+    w = gen.fwd_inputs(512, 16, 256, 256, 64, "bf16", seed=9310, causal=True, kv_len_range=(1, 256))
+    o, lse = gpu_forward(w)
+    o_ref, lse_ref = oracle.attention_fwd(w.q, w.k, w.v, w.dtype, w.scale, w.causal, w.kv_lens,
+                                          nthreads=host_cores())
+    print("head groups B512 H16 N256", compare(o, lse, o_ref, lse_ref, "eight head groups"), flush=True)
+
+
 # ------------------------------------------------ ragged and edge shapes
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,causal,lens", [
